@@ -1,0 +1,157 @@
+/* nvfp4v: NVFP4 skinny verify-GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The operation. A speculative-decoding verify pass applies every linear layer
+ * of the target model to all rows of a draft tree in one forward pass; the
+ * weights are stored with four bits per weight and one scale per 16 weights,
+ * so the pass is a skinny GEMM that streams 4-bit weights from HBM and whose
+ * cost is flat in the row count until a tile boundary is crossed
+ * (TandemLLM manual, "What TandemLLM is", 1.2 "Two levers"; StairCut research
+ * page, "What it says"). This library computes, for M = 1..64 rows,
+ *
+ *     C[M, N] (fp32) = ts * A[M, K] (bf16) * W[N, K]^T,
+ *     W[j, k] = E2M1(code[j, k]) * E4M3(scale[j, k / 16])
+ *
+ * Reading of the format (the pages give only "4 bits, one scale per 16"):
+ * E2M1 codes (sign, 2-bit exponent with bias 1, 1 mantissa bit: magnitudes
+ * 0, .5, 1, 1.5, 2, 3, 4, 6), an OCP E4M3 ("FN": bias 7, no infinities,
+ * 0x7F/0xFF are NaN) scale for every 16 consecutive elements along K, and an
+ * fp32 tensor scale ts.
+ *
+ * Canonical (interchange) format, row-major, caller-owned:
+ *     codes  uint8 [N][K/2]   byte b of row j holds k = 2b (low nibble) and
+ *                             k = 2b + 1 (high nibble)
+ *     scales uint8 [N][K/16]  E4M3 byte of block k/16
+ * Packed (device) format: an opaque byte permutation of the canonical bytes,
+ * zero-padded to N % 16 == 0 and K % 128 == 0, produced by nvfp4v_pack() and
+ * consumed by nvfp4v_verify_gemm(); its size is nvfp4v_packed_bytes(). When
+ * N % 16 == 0 and K % 128 == 0 it is exactly N*K/2 + N*K/16 bytes.
+ *
+ * Conventions for every call:
+ *   - "dev" pointers are device memory on the context's GPU, "host" pointers
+ *     are host memory. The caller owns every buffer it passes in.
+ *   - Sizes are element counts (int64_t), never bytes unless named *_bytes.
+ *   - Return 0 on success or a negative NVFP4V_E_* status. All argument checks
+ *     run on the host before any HIP call; on error nothing is launched and
+ *     no output is written. No C++ exception crosses this interface.
+ *   - Calls that take a hipStream_t enqueue work and return without
+ *     synchronising; faults during execution surface at the caller's next
+ *     synchronisation. Launch failures return NVFP4V_E_HIP and the hipError_t
+ *     is kept (nvfp4v_last_hip_error).
+ *   - Calls that share one context must not run concurrently (they share the
+ *     context's split-K workspace); enqueue them on one stream.
+ *   - The K-reduction order is fixed for a given (N, K, M, device): repeated
+ *     calls return bitwise identical C (TandemLLM manual, 1.7 "The paper":
+ *     the 4-bit kernels keep a fixed reduction order).
+ */
+#ifndef NVFP4V_H
+#define NVFP4V_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4V_OK 0
+#define NVFP4V_E_INVALID_ARG (-1) /* null pointer / null context / bad enum   */
+#define NVFP4V_E_SHAPE (-2)       /* K % 16 != 0, N < 1, K < 16, too large     */
+#define NVFP4V_E_M_RANGE (-3)     /* M < 1 or M > NVFP4V_MAX_M                  */
+#define NVFP4V_E_ALIGN (-4)       /* a device pointer is not 16-byte aligned   */
+#define NVFP4V_E_HIP (-5)         /* a HIP runtime or launch error             */
+#define NVFP4V_E_FAULT (-6)       /* injected by NVFP4V_FAULT=launch (testing) */
+#define NVFP4V_E_NONFINITE (-7)   /* quantiser input holds NaN or Inf          */
+#define NVFP4V_E_WORKSPACE (-8)   /* the request exceeds the context workspace */
+
+#define NVFP4V_MAX_M 64
+
+typedef struct nvfp4v_ctx nvfp4v_ctx;
+
+/* Create a context on HIP device `device` (>= 0). It holds the device's
+ * properties, the tile table, and a split-K workspace (partial sums and
+ * arrival counters) allocated here once, so that nvfp4v_verify_gemm never
+ * allocates and can be captured in a HIP graph. The caller destroys it. */
+int nvfp4v_create(nvfp4v_ctx **out, int device);
+void nvfp4v_destroy(nvfp4v_ctx *ctx);
+
+/* Human-readable text for a status code (static storage). */
+const char *nvfp4v_strerror(int status);
+/* The hipError_t behind the last NVFP4V_E_HIP on this context (0 if none). */
+int nvfp4v_last_hip_error(const nvfp4v_ctx *ctx);
+
+/* ---- Format ------------------------------------------------------------ */
+
+/* Quantise fp32 host weights w[N][K] to the canonical format (host buffers
+ * codes[N][K/2], scales[N][K/16]). Per 16-element block along K:
+ *     s = E4M3_RNE(absmax / 6)    (fp64, round to nearest even, saturating
+ *                                   at 448; may be 0)
+ *     code = s == 0 ? +0 : E2M1_RNE(w / s)   (fp64, ties to the even mantissa,
+ *                                   saturating at 6, sign kept so tiny
+ *                                   negatives become -0)
+ * The pages say only that the weights were quantised onto the NVFP4 grid
+ * ("Installing TandemLLM", 3.12); this absmax/6 rule is the plain reading.
+ * Errors: INVALID_ARG, SHAPE (K % 16, N < 1), NONFINITE. */
+int nvfp4v_quantize_host(const float *w_host, int64_t n, int64_t k, uint8_t *codes_host,
+                         uint8_t *scales_host);
+
+/* The same quantiser on the GPU: w_dev fp32 [N][K] -> codes_dev [N][K/2],
+ * scales_dev [N][K/16], byte-identical to nvfp4v_quantize_host. Non-finite
+ * weights are not reported on this path (the bytes are then unspecified);
+ * check inputs on the host if they can hold NaN/Inf. */
+int nvfp4v_quantize(nvfp4v_ctx *ctx, const float *w_dev, int64_t n, int64_t k,
+                    uint8_t *codes_dev, uint8_t *scales_dev, hipStream_t stream);
+
+/* Round fp32 host values to E4M3 bytes (nearest even, saturating at +-448,
+ * NaN rejected with NONFINITE). Used to store scale values given directly. */
+int nvfp4v_encode_e4m3_host(const float *x_host, int64_t count, uint8_t *out_host);
+
+/* Bytes of the packed (device) format for an N x K matrix. 0 for bad shapes. */
+size_t nvfp4v_packed_bytes(int64_t n, int64_t k);
+
+/* Canonical (device buffers) -> packed (device buffer of nvfp4v_packed_bytes).
+ * Padding bytes are written as zero codes with zero scales.
+ * Errors: INVALID_ARG, SHAPE, ALIGN (packed_dev), HIP. */
+int nvfp4v_pack(nvfp4v_ctx *ctx, const uint8_t *codes_dev, const uint8_t *scales_dev, int64_t n,
+                int64_t k, void *packed_dev, hipStream_t stream);
+
+/* Packed -> canonical (inverse of nvfp4v_pack). */
+int nvfp4v_unpack(nvfp4v_ctx *ctx, const void *packed_dev, int64_t n, int64_t k,
+                  uint8_t *codes_dev, uint8_t *scales_dev, hipStream_t stream);
+
+/* ---- The verify GEMM ---------------------------------------------------- */
+
+/* C[M][N] = ts * A[M][K] * W[N][K]^T.
+ *   a_dev      bf16 bit patterns, row-major [M][K] (row stride K), 16-byte
+ *              aligned, K % 8 == 0 for that alignment to hold per row
+ *   packed_dev nvfp4v_pack output for the N x K weights, 16-byte aligned
+ *   c_dev      fp32, row-major [M][N], 16-byte aligned; fully overwritten
+ * M in 1..64. Does not allocate; safe to capture in a HIP graph.
+ * Errors: INVALID_ARG, SHAPE, M_RANGE, ALIGN, WORKSPACE, HIP, FAULT. */
+int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_t k,
+                       const void *packed_dev, int64_t n, float ts, float *c_dev,
+                       hipStream_t stream);
+
+/* The kernel variant and tiling the tile table picks for (N, K, M): writes a
+ * short description into buf (NUL-terminated, truncated to len). */
+int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64_t m, char *buf, size_t len);
+
+/* ---- Staircase sweep ---------------------------------------------------- */
+
+/* Measure the verify GEMM's duration for every M in [m_lo, m_hi] on an N x K
+ * weight matrix (the per-M cost "staircase" that StairCut prices; StairCut
+ * research page, "What it says"). The call allocates its own buffers:
+ * max(1, ceil(rotate_bytes / packed)) weight copies filled with valid random
+ * codes and scales, cycled so timing does not hit a cache-resident copy; it
+ * runs `warmup` untimed launches, then `reps` launches each between a pair of
+ * HIP events on an internal stream, and writes the median duration in
+ * microseconds to us_out[M - m_lo]. Synchronous. */
+int nvfp4v_staircase(nvfp4v_ctx *ctx, int64_t n, int64_t k, int m_lo, int m_hi, int warmup,
+                     int reps, size_t rotate_bytes, double *us_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4V_H */

@@ -1,0 +1,176 @@
+// Internal declarations of the nvfp4v library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/nvfp4v.h"
+
+// ---------------------------------------------------------------------------
+// Packed (device) layout.
+//
+// The weight matrix is cut into row tiles of 16 rows. Each row tile is one
+// contiguous stripe covering all of K, cut into k-tiles of 128 elements, and
+// the k-tiles are grouped in super-groups of up to 8:
+//
+//   stripe(rt)      = rt * nkt * TILE_BYTES
+//   super-group g   = stripe + g * 8 * TILE_BYTES, holding q = min(8, nkt - 8g)
+//                     k-tiles as [q x 1024 code bytes][q x 128 scale bytes]
+//   code tile t     : 1024 bytes; lane L = r + 16h (r = row in tile, h = 0..3)
+//                     owns bytes [16L, 16L + 16) = the 32 codes of row r for
+//                     k in [128 kt + 32h, 128 kt + 32h + 32), canonical order
+//                     (byte b: low nibble k = 2b, high nibble 2b + 1)
+//   scale block     : lane L owns bytes [2qL, 2qL + 2q); byte 2t + e is the
+//                     E4M3 scale of row r, 16-block 8 kt + 2h + e (kt = 8g + t)
+//
+// One wave reads a code tile with one 16-byte load per lane (1 KiB fully
+// contiguous per wave), and the lane's 32 codes are exactly what it feeds to
+// four 16x16x32 MFMAs (8 consecutive k per MFMA). Each byte of the canonical
+// format appears once; padding (rows >= N, k >= K) is zero codes / zero
+// scales, so it contributes exact zeros.
+// ---------------------------------------------------------------------------
+namespace nvfp4v {
+
+constexpr int ROWS_PER_TILE = 16;
+constexpr int K_PER_TILE = 128;
+constexpr int CODE_TILE_BYTES = 1024;
+constexpr int SCALE_TILE_BYTES = 128;
+constexpr int TILE_BYTES = CODE_TILE_BYTES + SCALE_TILE_BYTES;  // 1152
+constexpr int TILES_PER_GROUP = 8;
+
+struct Layout {
+  int64_t n, k;
+  int64_t nrt;  // row tiles
+  int64_t nkt;  // k tiles
+  size_t bytes() const { return (size_t)nrt * (size_t)nkt * TILE_BYTES; }
+};
+
+inline bool make_layout(int64_t n, int64_t k, Layout *L) {
+  if (n < 1 || k < 16 || k % 16 != 0) return false;
+  if (n > (int64_t(1) << 31) || k > (int64_t(1) << 24)) return false;
+  L->n = n;
+  L->k = k;
+  L->nrt = (n + ROWS_PER_TILE - 1) / ROWS_PER_TILE;
+  L->nkt = (k + K_PER_TILE - 1) / K_PER_TILE;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Format encoders shared by the host and device quantisers (product side).
+// ---------------------------------------------------------------------------
+
+// Round a finite, non-negative double to the nearest E4M3 magnitude (ties to
+// even), saturating at 448, by integer rounding of the fp64 significand.
+__host__ __device__ inline uint32_t e4m3_encode_mag(double x) {
+  if (!(x < 448.0)) return 0x7E;
+  uint64_t bits;
+  memcpy(&bits, &x, 8);
+  const int bexp = (int)((bits >> 52) & 0x7FF);
+  if (bexp == 0) return 0;  // zero or fp64 subnormal: far below 2^-10
+  const int e = bexp - 1023;
+  uint64_t sig = (bits & ((uint64_t(1) << 52) - 1)) | (uint64_t(1) << 52);  // value = sig * 2^(e-52)
+  // Target grid step: 2^(e-3) for e >= -6 (3 stored mantissa bits), 2^-9 below.
+  const int step = e >= -6 ? e - 3 : -9;
+  const int shift = step - (e - 52);  // drop `shift` low bits of sig
+  if (shift > 60) return 0;           // below half of 2^-9: rounds to 0
+  const uint64_t q = sig >> shift;
+  const uint64_t rem = sig & ((uint64_t(1) << shift) - 1);
+  const uint64_t half = uint64_t(1) << (shift - 1);
+  uint64_t r = q + ((rem > half || (rem == half && (q & 1))) ? 1 : 0);
+  // r is the value in units of 2^step.
+  if (e < -6) return (uint32_t)r;  // 0..8 (8 = 2^-6, the same bit pattern as e=1,m=0)
+  int ef = e + 7;
+  if (r == 16) {
+    r = 8;
+    ef += 1;
+  }
+  const uint32_t out = ((uint32_t)ef << 3) | (uint32_t)(r - 8);
+  return out > 0x7E ? 0x7E : out;
+}
+
+__host__ __device__ inline double e4m3_decode_f64(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  double v;
+  if (e == 15 && m == 7) return __builtin_nan("");
+  if (e == 0)
+    v = (double)m * (1.0 / 512.0);
+  else {
+    // 2^(e-7) * (8 + m) / 8
+    uint64_t bits = ((uint64_t)(e - 7 + 1023) << 52) | ((uint64_t)m << 49);
+    memcpy(&v, &bits, 8);
+  }
+  return (b & 0x80) ? -v : v;
+}
+
+// E2M1 round-to-nearest (ties to the even mantissa), saturating at 6, sign kept.
+__host__ __device__ inline uint32_t e2m1_encode(double q) {
+  const uint32_t sgn = __builtin_signbit(q) ? 8u : 0u;
+  const double a = q < 0 ? -q : q;
+  uint32_t c;
+  if (a <= 0.25) c = 0;
+  else if (a < 0.75) c = 1;
+  else if (a <= 1.25) c = 2;
+  else if (a < 1.75) c = 3;
+  else if (a <= 2.5) c = 4;
+  else if (a < 3.5) c = 5;
+  else if (a <= 5.0) c = 6;
+  else c = 7;
+  return c | sgn;
+}
+
+// Quantise one 16-element block: writes 8 code bytes and returns the scale byte.
+__host__ __device__ inline uint32_t quantize_block(const float *w, uint8_t *codes8) {
+  double amax = 0.0;
+  for (int t = 0; t < 16; ++t) {
+    const double a = w[t] < 0 ? -(double)w[t] : (double)w[t];
+    amax = a > amax ? a : amax;
+  }
+  const uint32_t sb = e4m3_encode_mag(amax / 6.0);
+  const double s = e4m3_decode_f64(sb);
+  for (int b = 0; b < 8; ++b) {
+    uint32_t lo = 0, hi = 0;
+    if (s != 0.0) {
+      lo = e2m1_encode((double)w[2 * b] / s);
+      hi = e2m1_encode((double)w[2 * b + 1] / s);
+    }
+    codes8[b] = (uint8_t)(lo | (hi << 4));
+  }
+  return sb;
+}
+
+// ---------------------------------------------------------------------------
+// Context.
+// ---------------------------------------------------------------------------
+struct Plan {
+  int variant;      // 0 = MFMA bf16
+  int mblocks;      // ceil(M / 16)
+  int waves;        // waves per work-group
+  int row_tiles_per_wg;
+  int ksplit;       // work-groups along K
+  int ktiles_per_split;
+  int ktiles_per_chunk;  // k-tiles of activations staged in LDS at a time
+  int grid_x, grid_y;
+  size_t lds_bytes;
+};
+
+}  // namespace nvfp4v
+
+struct nvfp4v_ctx {
+  int device = 0;
+  int num_cus = 0;
+  int last_hip = 0;
+  float *partials = nullptr;  // split-K partial sums
+  size_t partial_floats = 0;
+  unsigned *counters = nullptr;  // per row-block arrival counters (kept at 0 between calls)
+  size_t n_counters = 0;
+};
+
+namespace nvfp4v {
+int fault_injected();  // NVFP4V_FAULT=launch
+int hip_status(nvfp4v_ctx *ctx, hipError_t e);
+bool aligned16(const void *p);
+int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p);
+}  // namespace nvfp4v

@@ -1,0 +1,120 @@
+// Staircase sweep: the verify GEMM's duration as a function of the row count
+// M, which is the price table StairCut cuts draft trees against (StairCut
+// research page, "What it says": the check's cost rises in steps when the row
+// count crosses a kernel tile boundary; release post: the staircase is
+// measured, not assumed).
+#include <algorithm>
+#include <vector>
+
+#include "internal.h"
+
+using namespace nvfp4v;
+
+namespace {
+
+__device__ inline uint32_t mix32(uint64_t x) {
+  x ^= x >> 33;
+  x *= 0xff51afd7ed558ccdULL;
+  x ^= x >> 33;
+  x *= 0xc4ceb9fe1a85ec53ULL;
+  x ^= x >> 33;
+  return (uint32_t)x;
+}
+
+// Fill `copies` packed matrices with random codes and finite scales in
+// [2^-3, 2^1] (bytes 0x20..0x40), so the sweep times real dequantisation.
+__global__ void k_fill_packed(uint8_t *buf, size_t copy_stride, int copies, int64_t nrt,
+                              int64_t nkt, uint64_t seed) {
+  const size_t per = (size_t)nrt * (size_t)nkt * TILE_BYTES;
+  const size_t total = per * (size_t)copies;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t c = i / per, off = i - c * per;
+    const size_t stripe = (size_t)nkt * TILE_BYTES;
+    const size_t in_stripe = off % stripe;
+    const size_t g = in_stripe / ((size_t)TILES_PER_GROUP * TILE_BYTES);
+    const size_t in_group = in_stripe - g * (size_t)TILES_PER_GROUP * TILE_BYTES;
+    const int64_t q = std::min<int64_t>(TILES_PER_GROUP, nkt - (int64_t)g * TILES_PER_GROUP);
+    const uint32_t r = mix32(seed ^ (i * 0x9E3779B97F4A7C15ULL));
+    uint8_t v = (uint8_t)r;
+    if (in_group >= (size_t)q * CODE_TILE_BYTES) v = (uint8_t)(0x20 + (r % 0x21));
+    buf[c * copy_stride + off] = v;
+  }
+}
+
+__global__ void k_fill_act(uint16_t *a, size_t count, uint64_t seed) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const uint32_t r = mix32(seed + i);
+    a[i] = (uint16_t)(0x3F00u | (r & 0x00FFu) | ((r >> 8) & 0x8000u));
+  }
+}
+
+}  // namespace
+
+extern "C" int nvfp4v_staircase(nvfp4v_ctx *ctx, int64_t n, int64_t k, int m_lo, int m_hi,
+                                int warmup, int reps, size_t rotate_bytes, double *us_out) {
+  if (!ctx || !us_out) return NVFP4V_E_INVALID_ARG;
+  if (m_lo < 1 || m_hi > NVFP4V_MAX_M || m_lo > m_hi) return NVFP4V_E_M_RANGE;
+  if (reps < 1 || warmup < 0) return NVFP4V_E_INVALID_ARG;
+  Layout L;
+  if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
+  if (fault_injected()) return NVFP4V_E_FAULT;
+  const size_t per = L.bytes();
+  const size_t stride = (per + 255) & ~size_t(255);
+  size_t copies = rotate_bytes > per ? (rotate_bytes + per - 1) / per : 1;
+  copies = std::min<size_t>(copies, 4096);
+
+  uint8_t *w = nullptr;
+  uint16_t *a = nullptr;
+  float *c = nullptr;
+  hipStream_t s = nullptr;
+  std::vector<hipEvent_t> ev((size_t)reps * 2, nullptr);
+  int rc = NVFP4V_OK;
+  hipError_t e = hipMalloc((void **)&w, stride * copies);
+  if (e == hipSuccess) e = hipMalloc((void **)&a, (size_t)NVFP4V_MAX_M * (size_t)k * 2);
+  if (e == hipSuccess) e = hipMalloc((void **)&c, (size_t)NVFP4V_MAX_M * (size_t)n * 4);
+  if (e == hipSuccess) e = hipStreamCreate(&s);
+  for (size_t i = 0; e == hipSuccess && i < ev.size(); ++i) e = hipEventCreate(&ev[i]);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(k_fill_packed, dim3(4096), dim3(256), 0, s, w, stride, (int)copies, L.nrt,
+                       L.nkt, 0x5EEDULL);
+    hipLaunchKernelGGL(k_fill_act, dim3(256), dim3(256), 0, s, a, (size_t)NVFP4V_MAX_M * (size_t)k,
+                       0xA11CEULL);
+    e = hipGetLastError();
+  }
+  size_t rot = 0;
+  for (int m = m_lo; e == hipSuccess && rc == NVFP4V_OK && m <= m_hi; ++m) {
+    for (int i = 0; i < warmup && rc == NVFP4V_OK; ++i, ++rot)
+      rc = nvfp4v_verify_gemm(ctx, a, m, k, w + (rot % copies) * stride, n, 1.0f, c, s);
+    for (int i = 0; i < reps && rc == NVFP4V_OK; ++i, ++rot) {
+      e = hipEventRecord(ev[2 * i], s);
+      if (e != hipSuccess) break;
+      rc = nvfp4v_verify_gemm(ctx, a, m, k, w + (rot % copies) * stride, n, 1.0f, c, s);
+      if (rc != NVFP4V_OK) break;
+      e = hipEventRecord(ev[2 * i + 1], s);
+      if (e != hipSuccess) break;
+    }
+    if (e == hipSuccess && rc == NVFP4V_OK) e = hipStreamSynchronize(s);
+    if (e == hipSuccess && rc == NVFP4V_OK) {
+      std::vector<double> t((size_t)reps);
+      for (int i = 0; i < reps && e == hipSuccess; ++i) {
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]);
+        t[(size_t)i] = 1000.0 * (double)ms;
+      }
+      std::sort(t.begin(), t.end());
+      us_out[m - m_lo] = reps % 2 ? t[(size_t)reps / 2]
+                                  : 0.5 * (t[(size_t)reps / 2 - 1] + t[(size_t)reps / 2]);
+    }
+  }
+  if (e != hipSuccess && rc == NVFP4V_OK) rc = hip_status(ctx, e);
+  if (s) (void)hipStreamSynchronize(s);
+  for (auto &x : ev)
+    if (x) (void)hipEventDestroy(x);
+  if (s) (void)hipStreamDestroy(s);
+  if (w) (void)hipFree(w);
+  if (a) (void)hipFree(a);
+  if (c) (void)hipFree(c);
+  return rc;
+}

@@ -1,0 +1,238 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element, on the
+same seeded inputs. Bar: |C_gpu - C| <= 1e-5 * sum_k |a w| per element (byte
+equality for the quantiser and the pack round trip, bitwise equality for
+determinism)."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import nvfp4_skinny_gemm_amd as nv
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+@pytest.fixture(scope="module")
+def ctx(torch_cuda):
+    c = nv.Context(0)
+    yield c
+    c.close()
+
+
+def to_dev(torch, arr):
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def bf16_dev(torch, a_bits):
+    return torch.from_numpy(np.ascontiguousarray(a_bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def pack_dev(torch, ctx, codes, scales, n, k):
+    return ctx.pack(to_dev(torch, codes), to_dev(torch, scales), n, k)
+
+
+def assert_parity(oracle, c_gpu, c_ref, s_ref, label):
+    ok = oracle.within_tolerance(c_gpu, c_ref, s_ref)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i, j = bad[0]
+        err = np.abs(c_gpu.astype(np.float64) - c_ref)
+        rel = np.where(s_ref > 0, err / np.maximum(s_ref, 1e-300), np.inf)
+        raise AssertionError(
+            "%s: %d of %d outside 1e-5*S; first at [%d,%d]: gpu=%r ref=%r S=%r; worst err/S=%g"
+            % (label, bad.shape[0], ok.size, i, j, float(c_gpu[i, j]), c_ref[i, j], s_ref[i, j],
+               float(np.nanmax(rel))))
+
+
+def tiny_inputs(oracle):
+    n, k = 512, 256
+    codes = synth.tiny_codes(n, k, seed=0)
+    svals = synth.tiny_scale_values(n, k, seed=0)
+    scales_prod = nv.encode_e4m3_host(svals)
+    scales_orc = np.array([oracle.e4m3_encode(float(v)) for v in svals.ravel()], np.uint8).reshape(svals.shape)
+    assert np.array_equal(scales_prod, scales_orc)
+    a = synth.activations_bf16(64, k, seed=0, outliers=False)
+    return n, k, codes, scales_prod, scales_orc, a
+
+
+def test_tiny_config_every_m(torch_cuda, ctx, oracle_mod):
+    torch = torch_cuda
+    n, k, codes, scales_p, scales_o, a = tiny_inputs(oracle_mod)
+    c_ref, s_ref = oracle_mod.gemm(a, codes, scales_o)
+    packed = pack_dev(torch, ctx, codes, scales_p, n, k)
+    a_dev = bf16_dev(torch, a)
+    for m in range(1, 65):
+        log("tiny 512x256 M=%d" % m)
+        c = ctx.verify_gemm(a_dev[:m], packed, n, k).cpu().numpy()
+        assert_parity(oracle_mod, c, c_ref[:m], s_ref[:m], "tiny M=%d" % m)
+
+
+def test_device_quantizer_matches_oracle(torch_cuda, ctx, oracle_mod):
+    torch = torch_cuda
+    for (n, k) in [(512, 256), (37, 1040), (1000, 5120)]:
+        log("quantize %dx%d" % (n, k))
+        w = synth.weights_f32(n, k, seed=0, stream="devq")
+        w[0, :16] = 0.0
+        w[1, :16] = np.float32(1e-5)
+        w[2, :16] = np.float32(5000.0)
+        w[3, :16] = -np.float32(1e-9)
+        w[3, 0] = 6.0
+        w[5, :16] *= np.float32(2.0 ** -12)
+        w[6, 16:32] = np.float32(6.375)
+        codes, scales = ctx.quantize(to_dev(torch, w))
+        oc, osc = oracle_mod.quantize(w)
+        assert np.array_equal(scales.cpu().numpy(), osc)
+        assert np.array_equal(codes.cpu().numpy(), oc)
+
+
+@pytest.mark.parametrize("n,k", [(1, 16), (17, 48), (512, 256), (33, 1040), (16, 128), (40, 2064)])
+def test_pack_roundtrip(torch_cuda, ctx, n, k):
+    torch = torch_cuda
+    g = np.random.default_rng(n * 7919 + k)
+    codes = g.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scales = g.integers(0, 256, (n, k // 16), dtype=np.uint8)
+    packed = pack_dev(torch, ctx, codes, scales, n, k)
+    assert packed.numel() == nv.packed_bytes(n, k)
+    c2, s2 = ctx.unpack(packed, n, k)
+    assert np.array_equal(c2.cpu().numpy(), codes)
+    assert np.array_equal(s2.cpu().numpy(), scales)
+    # padding is zero and every canonical byte appears exactly once
+    assert int((packed.cpu().numpy() != 0).sum()) <= codes.size + scales.size
+
+
+def random_codes_scales(g, n, k, lo=0x18, hi=0x50):
+    codes = g.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scales = g.integers(lo, hi, (n, k // 16), dtype=np.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("n,k", [(1, 16), (17, 48), (100, 144), (33, 1040), (64, 256), (48, 2176)])
+def test_edge_shapes(torch_cuda, ctx, oracle_mod, n, k):
+    torch = torch_cuda
+    g = np.random.default_rng(n * 131 + k)
+    codes, scales = random_codes_scales(g, n, k)
+    a = synth.activations_bf16(64, k, seed=1, outliers=False)
+    c_ref, s_ref = oracle_mod.gemm(a, codes, scales, ts=0.375)
+    packed = pack_dev(torch, ctx, codes, scales, n, k)
+    a_dev = bf16_dev(torch, a)
+    for m in (1, 5, 16, 17, 33, 64):
+        log("edge %dx%d M=%d" % (n, k, m))
+        c = ctx.verify_gemm(a_dev[:m], packed, n, k, ts=0.375).cpu().numpy()
+        assert_parity(oracle_mod, c, c_ref[:m], s_ref[:m], "edge %dx%d M=%d" % (n, k, m))
+
+
+def test_special_values(torch_cuda, ctx, oracle_mod):
+    torch = torch_cuda
+    n, k = 64, 512
+    g = np.random.default_rng(77)
+    codes, scales = random_codes_scales(g, n, k)
+    codes[0] = 0                   # all-zero row
+    codes[1] = 0x88                # all -0
+    scales[2] = 0x7E               # max scale 448
+    scales[3] = g.integers(1, 8, k // 16)  # subnormal scales
+    scales[4] = 0x00               # zero scales
+    scales[5, 3] = 0x7F            # NaN scale -> NaN outputs in column 5
+    a = synth.activations_bf16(64, k, seed=2, outliers=True)
+    c_ref, s_ref = oracle_mod.gemm(a, codes, scales, ts=2.5)
+    packed = pack_dev(torch, ctx, codes, scales, n, k)
+    for m in (1, 16, 64):
+        c = ctx.verify_gemm(bf16_dev(torch, a[:m]), packed, n, k, ts=2.5).cpu().numpy()
+        assert_parity(oracle_mod, c, c_ref[:m], s_ref[:m], "special M=%d" % m)
+        assert np.isnan(c[:, 5]).all()
+        assert (c[:, 0] == 0).all() and (c[:, 1] == 0).all() and (c[:, 4] == 0).all()
+
+
+def full_shape_case(torch, ctx, oracle_mod, n, k, ms, stream):
+    log("generate %dx%d" % (n, k))
+    w = synth.weights_f32(n, k, seed=0, stream=stream)
+    oc, osc = oracle_mod.quantize(w)
+    codes_d, scales_d = ctx.quantize(to_dev(torch, w))
+    assert np.array_equal(scales_d.cpu().numpy(), osc), "device quantiser scales differ"
+    assert np.array_equal(codes_d.cpu().numpy(), oc), "device quantiser codes differ"
+    del w
+    packed = ctx.pack(codes_d, scales_d, n, k)
+    a = synth.activations_bf16(max(ms), k, seed=0, stream=stream + "/act", outliers=True)
+    log("oracle %dx%d M=%d" % (n, k, max(ms)))
+    c_ref, s_ref = oracle_mod.gemm(a, oc, osc)
+    a_dev = bf16_dev(torch, a)
+    outs = {}
+    for m in ms:
+        log("gpu %dx%d M=%d  plan: %s" % (n, k, m, ctx.describe_plan(n, k, m)))
+        c = ctx.verify_gemm(a_dev[:m], packed, n, k).cpu().numpy()
+        assert_parity(oracle_mod, c, c_ref[:m], s_ref[:m], "%dx%d M=%d" % (n, k, m))
+        outs[m] = c
+    return packed, a_dev, outs
+
+
+def test_gate_up_projection_full(torch_cuda, ctx, oracle_mod):
+    full_shape_case(torch_cuda, ctx, oracle_mod, 17408, 5120, [1, 8, 16, 24, 32], "gate_up")
+
+
+def test_down_projection_full(torch_cuda, ctx, oracle_mod):
+    torch = torch_cuda
+    packed, a_dev, outs = full_shape_case(torch, ctx, oracle_mod, 5120, 17408, [1, 8, 16, 24, 32],
+                                          "down")
+    # determinism: the same call again is bitwise identical
+    for m in (1, 16, 32):
+        c2 = ctx.verify_gemm(a_dev[:m], packed, 5120, 17408).cpu().numpy()
+        assert np.array_equal(c2.view(np.uint32), outs[m].view(np.uint32)), "M=%d not deterministic" % m
+
+
+def test_lm_head_sampled(torch_cuda, ctx, oracle_mod):
+    """151936 x 5120: weights drawn on the GPU, the oracle checks 2048 sampled rows."""
+    torch = torch_cuda
+    n, k = 151936, 5120
+    log("generate head on the GPU")
+    w = synth.weights_f32_cuda(n, k, seed=0, stream="head")
+    codes_d, scales_d = ctx.quantize(w)
+    rows = np.sort(np.random.default_rng(9).choice(n, 2048, replace=False))
+    rows[-1] = n - 1
+    w_rows = w[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del w
+    oc, osc = oracle_mod.quantize(w_rows)
+    idx = torch.from_numpy(rows).cuda()
+    assert np.array_equal(codes_d[idx].cpu().numpy(), oc)
+    assert np.array_equal(scales_d[idx].cpu().numpy(), osc)
+    packed = ctx.pack(codes_d, scales_d, n, k)
+    del codes_d, scales_d
+    a = synth.activations_bf16(64, k, seed=0, stream="head/act", outliers=True)
+    c_ref, s_ref = oracle_mod.gemm(a, oc, osc)
+    a_dev = bf16_dev(torch, a)
+    for m in (1, 16, 17, 32, 64):
+        log("head M=%d plan: %s" % (m, ctx.describe_plan(n, k, m)))
+        c = ctx.verify_gemm(a_dev[:m], packed, n, k)
+        assert_parity(oracle_mod, c[:, idx].cpu().numpy(), c_ref[:m], s_ref[:m], "head M=%d" % m)
+
+
+def test_row_invariance(torch_cuda, ctx, oracle_mod):
+    torch = torch_cuda
+    n, k = 1024, 5120
+    g = np.random.default_rng(3)
+    codes, scales = random_codes_scales(g, n, k)
+    a = synth.activations_bf16(64, k, seed=4, outliers=True)
+    c_ref, s_ref = oracle_mod.gemm(a[:1], codes, scales)
+    packed = pack_dev(torch, ctx, codes, scales, n, k)
+    a_dev = bf16_dev(torch, a)
+    for m in (1, 2, 16, 31, 64):
+        c = ctx.verify_gemm(a_dev[:m], packed, n, k).cpu().numpy()
+        assert_parity(oracle_mod, c[:1], c_ref, s_ref, "row 0 at M=%d" % m)
+
+
+def test_staircase_runs(ctx):
+    us = ctx.staircase(512, 256, 1, 4, warmup=1, reps=3, rotate_bytes=0)
+    assert us.shape == (4,) and (us > 0).all()
