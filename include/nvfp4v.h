@@ -127,11 +127,29 @@ int nvfp4v_unpack(nvfp4v_ctx *ctx, const void *packed_dev, int64_t n, int64_t k,
  *              aligned, K % 8 == 0 for that alignment to hold per row
  *   packed_dev nvfp4v_pack output for the N x K weights, 16-byte aligned
  *   c_dev      fp32, row-major [M][N], 16-byte aligned; fully overwritten
- * M in 1..64. Does not allocate; safe to capture in a HIP graph.
+ * M in 1..64. Does not allocate; safe to capture in a HIP graph. Two kernels
+ * run: A is packed into the context's buffer (K up to 131072 at M = 64,
+ * else WORKSPACE), then the GEMM.
  * Errors: INVALID_ARG, SHAPE, M_RANGE, ALIGN, WORKSPACE, HIP, FAULT. */
 int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_t k,
                        const void *packed_dev, int64_t n, float ts, float *c_dev,
                        hipStream_t stream);
+
+/* Activations pre-packed in the GEMM's MFMA fragment order, for callers that
+ * produce the next GEMM's input themselves (the chained pass writes them from
+ * its glue kernels). nvfp4v_verify_gemm does this packing internally, into the
+ * context's buffer, before each call.
+ *   nvfp4v_act_packed_bytes: bytes of the packed form of A[M][K] (0 if bad).
+ *   nvfp4v_pack_activations: a_dev bf16 [M][K] row-major -> act_dev (16-byte
+ *     aligned, nvfp4v_act_packed_bytes bytes). Errors: INVALID_ARG, M_RANGE,
+ *     SHAPE, ALIGN, HIP, FAULT.
+ *   nvfp4v_verify_gemm_pa: as nvfp4v_verify_gemm, with A given packed. */
+size_t nvfp4v_act_packed_bytes(int64_t m, int64_t k);
+int nvfp4v_pack_activations(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_t k,
+                            void *act_dev, hipStream_t stream);
+int nvfp4v_verify_gemm_pa(nvfp4v_ctx *ctx, const void *act_dev, int64_t m, int64_t k,
+                          const void *packed_dev, int64_t n, float ts, float *c_dev,
+                          hipStream_t stream);
 
 /* The kernel variant and tiling the tile table picks for (N, K, M): writes a
  * short description into buf (NUL-terminated, truncated to len). */
@@ -149,6 +167,74 @@ int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64_t m, char 
  * microseconds to us_out[M - m_lo]. Synchronous. */
 int nvfp4v_staircase(nvfp4v_ctx *ctx, int64_t n, int64_t k, int m_lo, int m_hi, int warmup,
                      int reps, size_t rotate_bytes, double *us_out);
+
+
+/* ---- Full verify pass (chained layer stack) ----------------------------- */
+
+/* One layer of the dense stand-in stack. The pages give neither layer shapes
+ * nor the non-GEMM operations of the model (TandemLLM manual, "What TandemLLM
+ * is", 1.2 "Two levers"; 1.4 "What runs today"), so the pass is a uniform
+ * stack of the projections a dense layer streams, each packed with
+ * nvfp4v_pack:
+ *   qkv     [3H x H]  q, k and v stacked along N (rows 0..H-1 are q, ...)
+ *   o       [H x H]
+ *   gate_up [2I x H]  gate rows 0..I-1, then up rows
+ *   down    [H x I]
+ * with one fp32 tensor scale per packed matrix. */
+typedef struct nvfp4v_layer {
+  const void *qkv;
+  const void *o;
+  const void *gate_up;
+  const void *down;
+  float ts_qkv, ts_o, ts_gate_up, ts_down;
+} nvfp4v_layer;
+
+/* Elementwise chain glue, fp32 arithmetic, result rounded to bf16 (nearest
+ * even); x/y are fp32 [rows][ld], out is bf16 [rows][cols] (dense).
+ *   glue_scale: out = bf16(x * c)
+ *   glue_sum:   out = bf16(x * c + y * c)   (no fused multiply-add) */
+int nvfp4v_glue_scale(nvfp4v_ctx *ctx, const float *x_dev, int64_t ldx, int64_t rows, int64_t cols,
+                      float c, uint16_t *out_dev, hipStream_t stream);
+int nvfp4v_glue_sum(nvfp4v_ctx *ctx, const float *x_dev, int64_t ldx, const float *y_dev,
+                    int64_t ldy, int64_t rows, int64_t cols, float c, uint16_t *out_dev,
+                    hipStream_t stream);
+
+/* Bytes of caller-owned device workspace nvfp4v_verify_pass needs (0 for bad
+ * arguments): the fp32 outputs and bf16 inputs of one layer, plus two bf16
+ * hidden-state buffers. */
+size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter);
+
+/* Enqueue the whole pass on `stream`: for each layer, with c_h = H^-1/2,
+ * c_2 = (2H)^-1/2 and c_i = I^-1/2 (fp32, rounded from fp64):
+ *   qkv = GEMM(h, qkv);          o_in = glue_scale(v part of qkv, c_h)
+ *   o   = GEMM(o_in, o);         g_in = glue_scale(o, c_h)
+ *   gu  = GEMM(g_in, gate_up);   d_in = glue_sum(gate part, up part, c_2)
+ *   d   = GEMM(d_in, down);      h    = glue_scale(d, c_i)
+ * h0 is bf16 [M][H]; the last layer's h goes to h_out (bf16 [M][H]). If trace
+ * is not NULL, layer l's output h is also copied to trace[l][M][H]. Every
+ * glue map is linear, so activations keep an O(1) RMS over the stack. After the
+ * call returns, the workspace holds the last layer's fp32 GEMM outputs
+ * (qkv [M][3H] at offset 0, then o, gu, d, each 256-byte aligned).
+ * Does not allocate or synchronise; safe to capture in a HIP graph.
+ * Errors: INVALID_ARG, SHAPE (H or I not a multiple of 16), M_RANGE, ALIGN,
+ * WORKSPACE, HIP, FAULT. */
+int nvfp4v_verify_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_t hidden,
+                       int64_t inter, const uint16_t *h0_dev, int64_t m, void *ws_dev,
+                       size_t ws_bytes, uint16_t *h_out_dev, uint16_t *trace_dev,
+                       hipStream_t stream);
+
+/* ---- Measurement helpers ------------------------------------------------- */
+
+/* Stream `bytes` (multiple of 16, 16-byte aligned) from HBM with 16-byte loads
+ * and fold them into sink_dev (nvfp4v_read_probe_sink_words() words): the
+ * practical read ceiling the GEMM's bandwidth is compared with. */
+size_t nvfp4v_read_probe_sink_words(nvfp4v_ctx *ctx);
+int nvfp4v_read_probe(nvfp4v_ctx *ctx, const void *buf_dev, size_t bytes, uint32_t *sink_dev,
+                      hipStream_t stream);
+/* Plain device copy of `bytes` (a kernel of known traffic, for calibrating
+ * hardware byte counters). */
+int nvfp4v_copy_probe(nvfp4v_ctx *ctx, const void *src_dev, void *dst_dev, size_t bytes,
+                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -62,9 +62,22 @@ def load():
     lib.nvfp4v_pack.argtypes = [p, p, p, i64, i64, p, p]
     lib.nvfp4v_unpack.argtypes = [p, p, i64, i64, p, p, p]
     lib.nvfp4v_verify_gemm.argtypes = [p, p, i64, i64, p, i64, c.c_float, p, p]
+    lib.nvfp4v_act_packed_bytes.argtypes = [i64, i64]
+    lib.nvfp4v_act_packed_bytes.restype = c.c_size_t
+    lib.nvfp4v_pack_activations.argtypes = [p, p, i64, i64, p, p]
+    lib.nvfp4v_verify_gemm_pa.argtypes = [p, p, i64, i64, p, i64, c.c_float, p, p]
     lib.nvfp4v_describe_plan.argtypes = [p, i64, i64, i64, c.c_char_p, c.c_size_t]
     lib.nvfp4v_staircase.argtypes = [p, i64, i64, c.c_int, c.c_int, c.c_int, c.c_int,
                                      c.c_size_t, p]
+    lib.nvfp4v_glue_scale.argtypes = [p, p, i64, i64, i64, c.c_float, p, p]
+    lib.nvfp4v_glue_sum.argtypes = [p, p, i64, p, i64, i64, i64, c.c_float, p, p]
+    lib.nvfp4v_pass_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.nvfp4v_pass_workspace_bytes.restype = c.c_size_t
+    lib.nvfp4v_verify_pass.argtypes = [p, p, c.c_int, i64, i64, p, i64, p, c.c_size_t, p, p, p]
+    lib.nvfp4v_read_probe_sink_words.argtypes = [p]
+    lib.nvfp4v_read_probe_sink_words.restype = c.c_size_t
+    lib.nvfp4v_read_probe.argtypes = [p, p, c.c_size_t, p, p]
+    lib.nvfp4v_copy_probe.argtypes = [p, p, p, c.c_size_t, p]
     _lib = lib
     return lib
 
@@ -96,6 +109,10 @@ def _stream_handle(stream):
 
 def packed_bytes(n: int, k: int) -> int:
     return int(load().nvfp4v_packed_bytes(int(n), int(k)))
+
+
+def act_packed_bytes(m: int, k: int) -> int:
+    return int(load().nvfp4v_act_packed_bytes(int(m), int(k)))
 
 
 def quantize_host(w):
@@ -193,6 +210,77 @@ class Context:
                "nvfp4v_verify_gemm")
         return out
 
+    def pack_activations(self, a, k: int = None, out=None, stream=None):
+        """bf16 cuda tensor a[m, k] -> packed activations (uint8 cuda tensor)."""
+        import torch
+
+        m, k = a.shape
+        if out is None:
+            out = torch.empty(act_packed_bytes(m, k), dtype=torch.uint8, device=a.device)
+        _check(load().nvfp4v_pack_activations(self._h, _t_ptr(a), m, k, _t_ptr(out),
+                                              _stream_handle(stream)), "nvfp4v_pack_activations")
+        return out
+
+    def verify_gemm_pa(self, act, m: int, k: int, packed, n: int, ts: float = 1.0, out=None,
+                       stream=None):
+        """verify_gemm with activations already packed by pack_activations."""
+        import torch
+
+        if out is None:
+            out = torch.empty((m, n), dtype=torch.float32, device=act.device)
+        _check(load().nvfp4v_verify_gemm_pa(self._h, _t_ptr(act), m, k, _t_ptr(packed), n,
+                                            float(ts), _t_ptr(out), _stream_handle(stream)),
+               "nvfp4v_verify_gemm_pa")
+        return out
+
+    # -- chain glue and the full pass ---------------------------------------
+    def glue_scale(self, x, c: float, out=None, stream=None):
+        """bf16(x * c) for an fp32 cuda tensor x[rows, cols] (row stride x.stride(0))."""
+        import torch
+
+        rows, cols = x.shape
+        if out is None:
+            out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+        _check(load().nvfp4v_glue_scale(self._h, _t_ptr(x), x.stride(0), rows, cols, float(c),
+                                        _t_ptr(out), _stream_handle(stream)), "nvfp4v_glue_scale")
+        return out
+
+    def glue_sum(self, x, y, c: float, out=None, stream=None):
+        """bf16(x * c + y * c) for fp32 cuda tensors of one shape (no fused multiply-add)."""
+        import torch
+
+        rows, cols = x.shape
+        if out is None:
+            out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+        _check(load().nvfp4v_glue_sum(self._h, _t_ptr(x), x.stride(0), _t_ptr(y), y.stride(0),
+                                      rows, cols, float(c), _t_ptr(out), _stream_handle(stream)),
+               "nvfp4v_glue_sum")
+        return out
+
+    def verify_pass(self, layers, hidden: int, inter: int, h0, ws, h_out, trace=None,
+                    stream=None):
+        """Enqueue the chained pass; layers is a ctypes array of Layer."""
+        m = h0.shape[0]
+        _check(load().nvfp4v_verify_pass(
+            self._h, ctypes.cast(layers, ctypes.c_void_p), len(layers), hidden, inter,
+            _t_ptr(h0), m, _t_ptr(ws), ws.numel() * ws.element_size(), _t_ptr(h_out),
+            _t_ptr(trace) if trace is not None else None, _stream_handle(stream)),
+            "nvfp4v_verify_pass")
+        return h_out
+
+    # -- measurement helpers ------------------------------------------------
+    def read_probe(self, buf, sink, stream=None):
+        _check(load().nvfp4v_read_probe(self._h, _t_ptr(buf), buf.numel() * buf.element_size(),
+                                        _t_ptr(sink), _stream_handle(stream)), "nvfp4v_read_probe")
+
+    def read_probe_sink_words(self) -> int:
+        return int(load().nvfp4v_read_probe_sink_words(self._h))
+
+    def copy_probe(self, src, dst, stream=None):
+        nb = src.numel() * src.element_size()
+        _check(load().nvfp4v_copy_probe(self._h, _t_ptr(src), _t_ptr(dst), nb,
+                                        _stream_handle(stream)), "nvfp4v_copy_probe")
+
     def describe_plan(self, n: int, k: int, m: int) -> str:
         buf = ctypes.create_string_buffer(256)
         _check(load().nvfp4v_describe_plan(self._h, n, k, m, buf, 256), "nvfp4v_describe_plan")
@@ -206,6 +294,18 @@ class Context:
         _check(load().nvfp4v_staircase(self._h, n, k, m_lo, m_hi, warmup, reps, rotate_bytes,
                                        _np_ptr(out)), "nvfp4v_staircase")
         return out
+
+
+class Layer(ctypes.Structure):
+    """struct nvfp4v_layer: packed device pointers of one layer and their tensor scales."""
+
+    _fields_ = [("qkv", ctypes.c_void_p), ("o", ctypes.c_void_p), ("gate_up", ctypes.c_void_p),
+                ("down", ctypes.c_void_p), ("ts_qkv", ctypes.c_float), ("ts_o", ctypes.c_float),
+                ("ts_gate_up", ctypes.c_float), ("ts_down", ctypes.c_float)]
+
+
+def pass_workspace_bytes(m: int, hidden: int, inter: int) -> int:
+    return int(load().nvfp4v_pass_workspace_bytes(m, hidden, inter))
 
 
 def exported_names():

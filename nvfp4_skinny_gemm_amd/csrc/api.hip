@@ -28,6 +28,9 @@ using namespace nvfp4v;
 // row-block counters. The tile table keeps ksplit * M * N_pad within it.
 static constexpr size_t kPartialFloats = size_t(8) << 20;
 static constexpr size_t kCounters = 4096;
+// Packed-activation buffer of nvfp4v_verify_gemm: 16 MiB covers M = 64 up to
+// K = 131072 (larger requests return NVFP4V_E_WORKSPACE).
+static constexpr size_t kActBytes = size_t(16) << 20;
 
 extern "C" int nvfp4v_create(nvfp4v_ctx **out, int device) {
   if (!out || device < 0) return NVFP4V_E_INVALID_ARG;
@@ -41,6 +44,7 @@ extern "C" int nvfp4v_create(nvfp4v_ctx **out, int device) {
   if (e == hipSuccess) e = hipMalloc((void **)&ctx->partials, kPartialFloats * sizeof(float));
   if (e == hipSuccess) e = hipMalloc((void **)&ctx->counters, kCounters * sizeof(unsigned));
   if (e == hipSuccess) e = hipMemset(ctx->counters, 0, kCounters * sizeof(unsigned));
+  if (e == hipSuccess) e = hipMalloc((void **)&ctx->act, kActBytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     int code = (int)e;
@@ -50,6 +54,7 @@ extern "C" int nvfp4v_create(nvfp4v_ctx **out, int device) {
   }
   ctx->partial_floats = kPartialFloats;
   ctx->n_counters = kCounters;
+  ctx->act_bytes = kActBytes;
   *out = ctx;
   return NVFP4V_OK;
 }
@@ -58,6 +63,7 @@ extern "C" void nvfp4v_destroy(nvfp4v_ctx *ctx) {
   if (!ctx) return;
   if (ctx->partials) (void)hipFree(ctx->partials);
   if (ctx->counters) (void)hipFree(ctx->counters);
+  if (ctx->act) (void)hipFree(ctx->act);
   delete ctx;
 }
 

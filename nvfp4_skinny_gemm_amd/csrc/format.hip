@@ -94,8 +94,8 @@ extern "C" int nvfp4v_quantize(nvfp4v_ctx *ctx, const float *w, int64_t n, int64
   return hip_status(ctx, hipGetLastError());
 }
 
-// Pack: one thread per (row tile, k tile, lane) writes that lane's 16 code
-// bytes and its two scale bytes.
+// Pack: one thread per (row tile, k tile, lane) writes that lane's 32 code
+// bytes (two 16-byte halves) and its 4 scale bytes.
 __global__ void k_pack(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                        int64_t n, int64_t k, int64_t nrt, int64_t nkt, uint8_t *__restrict__ out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -105,21 +105,19 @@ __global__ void k_pack(const uint8_t *__restrict__ codes, const uint8_t *__restr
   const int64_t rt = tile / nkt, kt = tile - rt * nkt;
   const int r = L & 15, h = L >> 4;
   const int64_t row = rt * ROWS_PER_TILE + r;
-  const int64_t g = kt / TILES_PER_GROUP, t = kt - g * TILES_PER_GROUP;
-  const int64_t q = (nkt - g * TILES_PER_GROUP) < TILES_PER_GROUP ? (nkt - g * TILES_PER_GROUP)
-                                                                   : TILES_PER_GROUP;
-  uint8_t *grp = out + (rt * nkt + g * TILES_PER_GROUP) * (int64_t)TILE_BYTES;
-  uint8_t *cdst = grp + t * CODE_TILE_BYTES + L * 16;
+  uint8_t *t = out + tile * (int64_t)TILE_BYTES;
   const int64_t kb = k / 2;  // code bytes per row
-  for (int i = 0; i < 16; ++i) {
-    const int64_t byte = kt * 64 + h * 16 + i;
-    cdst[i] = (row < n && byte < kb) ? codes[row * kb + byte] : (uint8_t)0;
+  for (int c = 0; c < 2; ++c) {
+    uint8_t *dst = t + c * CODE_HALF_BYTES + L * 16;
+    for (int i = 0; i < 16; ++i) {
+      const int64_t byte = kt * 128 + h * 32 + c * 16 + i;
+      dst[i] = (row < n && byte < kb) ? codes[row * kb + byte] : (uint8_t)0;
+    }
   }
-  uint8_t *sdst = grp + q * CODE_TILE_BYTES + (int64_t)L * 2 * q + 2 * t;
   const int64_t sb = k / 16;
-  for (int e = 0; e < 2; ++e) {
-    const int64_t blk = kt * 8 + h * 2 + e;
-    sdst[e] = (row < n && blk < sb) ? scales[row * sb + blk] : (uint8_t)0;
+  for (int e = 0; e < 4; ++e) {
+    const int64_t blk = kt * 16 + h * 4 + e;
+    t[SCALE_OFFSET + L * 4 + e] = (row < n && blk < sb) ? scales[row * sb + blk] : (uint8_t)0;
   }
 }
 
@@ -132,16 +130,14 @@ __global__ void k_unpack(const uint8_t *__restrict__ in, int64_t n, int64_t k, i
   const int64_t row = idx / nb, blk = idx - row * nb;
   const int64_t rt = row / ROWS_PER_TILE;
   const int r = (int)(row - rt * ROWS_PER_TILE);
-  const int64_t kt = blk / 8;
-  const int h = (int)((blk % 8) / 2), e = (int)(blk % 2);
+  const int64_t kt = blk / 16;
+  const int q = (int)(blk % 16);  // 16-block within the k-tile = 4h + e
+  const int h = q / 4, e = q % 4;
   const int L = r + 16 * h;
-  const int64_t g = kt / TILES_PER_GROUP, t = kt - g * TILES_PER_GROUP;
-  const int64_t q = (nkt - g * TILES_PER_GROUP) < TILES_PER_GROUP ? (nkt - g * TILES_PER_GROUP)
-                                                                   : TILES_PER_GROUP;
-  const uint8_t *grp = in + (rt * nkt + g * TILES_PER_GROUP) * (int64_t)TILE_BYTES;
-  scales[row * nb + blk] = grp[q * CODE_TILE_BYTES + (int64_t)L * 2 * q + 2 * t + e];
-  // the block's 8 code bytes: canonical bytes blk*8 .. blk*8+7 = lane bytes e*8 .. e*8+7
-  const uint8_t *csrc = grp + t * CODE_TILE_BYTES + L * 16 + e * 8;
+  const uint8_t *t = in + (rt * nkt + kt) * (int64_t)TILE_BYTES;
+  scales[row * nb + blk] = t[SCALE_OFFSET + L * 4 + e];
+  // block e of the lane's 64 k = 8 code bytes: half c = e / 2, offset 8 * (e % 2)
+  const uint8_t *csrc = t + (e / 2) * CODE_HALF_BYTES + L * 16 + (e % 2) * 8;
   for (int i = 0; i < 8; ++i) codes[row * (k / 2) + blk * 8 + i] = csrc[i];
 }
 

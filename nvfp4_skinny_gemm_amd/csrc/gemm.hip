@@ -1,25 +1,39 @@
 // The verify GEMM: C[M][N] = ts * A[M][K] * W[N][K]^T with W in the packed
-// NVFP4 layout (internal.h), M = 1..64, on gfx950.
+// NVFP4 layout and A in packed (MFMA fragment) order (internal.h), M = 1..64,
+// on gfx950.
 //
-// Work decomposition. A work-group of 4 waves owns a row block of 4 row tiles
-// (64 weight rows) and one split of the k-tiles; each wave streams one row
-// tile across the split. The work-group stages the activations of the k-chunk
-// it is working on in LDS (all M rows, bf16), so each activation byte is read
-// from L2 once per work-group and reused by all four waves.
+// The pass is bound by streaming the 4-bit weights from HBM (TandemLLM manual,
+// "What TandemLLM is", 1.2 "Two levers": a verify pass over 16 rows reads the
+// same weights as one over a single row), so the kernel is organised around
+// keeping weight bytes in flight and everything else off the memory pipe:
 //
-// Per k-tile a lane loads its 16 code bytes and 2 scale bytes, dequantises
-// 8 codes at a time to bf16 (exact: an E2M1 value times an E4M3 scale has at
-// most 6 significant bits and lies in [2^-10, 2688]) and issues one
-// v_mfma_f32_16x16x32_bf16 per 8 codes and per 16-row block of M: the weights
-// are the MFMA's A operand (16 rows), the activations its B operand (16
-// columns), fp32 accumulation.
-//
-// Split-K. With ksplit > 1, every work-group writes its fp32 partial tile to
-// the context workspace and takes an arrival ticket; the last work-group of
-// the row block sums the partials in split order 0..ksplit-1 (a fixed order,
-// independent of arrival order; no float atomics) and writes C. This keeps the
-// K-reduction order fixed, as the pages require of the 4-bit kernels
-// (TandemLLM manual, "What TandemLLM is", 1.7 "The paper").
+//  * A work-group of 4 waves owns R row tiles (16 R weight rows) and one split
+//    of the k-tiles; its waves cut the split into 4 contiguous k-ranges. A wave
+//    walks its k-range; per k-tile it loads the activation fragments once
+//    (one coalesced 16-byte load per lane per fragment) and reuses them for
+//    all R row tiles, whose weight tiles stream through an R-deep register
+//    ring: after a row tile's k-tile is consumed, the same registers are
+//    refilled with that row tile's next k-tile, so about R tiles (R * 2304
+//    bytes per wave) are in flight while the wave computes.
+//  * Every load is an unconditional raw buffer load: a k-tile past the wave's
+//    range, a row tile past N or an activation row >= M gets an offset past the
+//    buffer's size, which returns zeros without a memory access. Straight-line
+//    loads keep the compiler's wait counts exact.
+//  * Dequantisation is exact: v_cvt_scalef32_pk_f32_fp4 turns two E2M1 codes
+//    into fp32 (with a unit scale; on gfx950 the instruction applies only the
+//    exponent of its scale operand), a fp32 multiply applies the E4M3 block
+//    scale (v_cvt_f32_fp8 decodes it), and the high halves are packed as bf16
+//    (an E2M1 value times an E4M3 scale has at most 6 significant bits and lies
+//    in [2^-10, 2688]).
+//  * v_mfma_f32_16x16x32_bf16 with the weights as the 16-row A operand and a
+//    16-row block of activations as the B operand, fp32 accumulation.
+//  * The 4 waves' tiles are summed through LDS in wave order. With ksplit > 1
+//    every work-group stores its partial tile with system-coherent stores
+//    (they bypass the non-coherent L2s of the other dies, so no L2 write-back
+//    fence is needed), waits for them, and takes an arrival ticket; the last
+//    work-group to arrive sums the partials in split order 0..ksplit-1. Both
+//    orders are fixed, so C is bitwise reproducible (TandemLLM manual, 1.7 "The
+//    paper": the 4-bit kernels keep a fixed reduction order). No float atomics.
 #include <algorithm>
 #include <cstdio>
 
@@ -33,26 +47,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int WG_THREADS = 256;
 constexpr int WG_WAVES = 4;
-constexpr int LDS_BUDGET = 40 * 1024;  // per work-group: 4 work-groups fit one CU's 160 KiB
-
-// E4M3 byte -> fp32, exact (NaN for 0x7F / 0xFF).
-__device__ inline float e4m3_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float v;
-  if (e == 0)
-    v = (float)m * 0.001953125f;  // m * 2^-9
-  else
-    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);
-  return (b & 0x80u) ? -v : v;
-}
+constexpr int WG_THREADS = 64 * WG_WAVES;
+constexpr int OOB = 0x7FFFFFF0;  // a buffer offset past every range: the load returns zeros
+constexpr int RAW_BUFFER_FLAGS = 0x00020000;
 
 template <int SEL>
 __device__ inline uint32_t dq_pair(uint32_t codes, float s) {
-  // Two E2M1 codes (byte SEL: low nibble = even k) -> two fp32, times s, then the
-  // high halves packed as bf16x2 (exact, the products fit bf16).
+  // Two E2M1 codes of byte SEL (low nibble = even k) -> fp32, times the block
+  // scale, high halves packed as bf16x2 (exact).
   const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, SEL);
   const float x = v.x * s, y = v.y * s;
   return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
@@ -69,158 +72,320 @@ __device__ inline bf16x8 dequant8(uint32_t codes, float s) {
   return r;
 }
 
-__device__ inline bf16x8 lds_b(const uint16_t *p) {
-  const uint4 v = *reinterpret_cast<const uint4 *>(p);
-  bf16x8 r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
+// The four E4M3 scale bytes of a lane -> fp32 (OCP E4M3 on gfx950, exact).
+__device__ inline void scales4(uint32_t sw, float s[4]) {
+  s[0] = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
+  s[1] = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
+  s[2] = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2);
+  s[3] = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
+}
+
+struct WTile {
+  uint4 c[2];  // code halves
+  uint32_t s;  // 4 scale bytes
+};
+
+// One row tile's k-tile (three loads per lane); `ok` false gives zeros.
+__device__ inline void load_wtile(WTile &t, __amdgpu_buffer_rsrc_t rs, int kt, bool ok, int lane) {
+  const int base = ok ? kt * TILE_BYTES : OOB;
+  const auto c0 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + lane * 16, 0, 0);
+  const auto c1 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + CODE_HALF_BYTES + lane * 16, 0, 0);
+  const auto sc = __builtin_amdgcn_raw_buffer_load_b32(rs, base + SCALE_OFFSET + lane * 4, 0, 0);
+  __builtin_memcpy(&t.c[0], &c0, 16);
+  __builtin_memcpy(&t.c[1], &c1, 16);
+  t.s = (uint32_t)sc;
+}
+
+// The 8 activation fragments of k-tile kt for each 16-row block (packed
+// activations); lanes whose row is >= M, or `ok` false, read zeros.
+template <int MB>
+__device__ inline void load_afrag(bf16x8 (&b)[MB][8], __amdgpu_buffer_rsrc_t ra, int kt, bool ok,
+                                  int M, int lane) {
+  const int col = lane & 15;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const bool v = ok && mb * 16 + col < M;
+    const int base = v ? (kt * MB + mb) * 8 * ACT_FRAG_BYTES + lane * 16 : OOB;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(ra, base + q * ACT_FRAG_BYTES, 0, 0);
+      __builtin_memcpy(&b[mb][q], &x, 16);
+    }
+  }
 }
 
 template <int MB>
-__global__ __launch_bounds__(WG_THREADS) void k_gemm_mfma(
-    const uint16_t *__restrict__ A, int M, int K, const uint8_t *__restrict__ W, int N, int nrt,
-    int nkt, int kts_per_split, int kts_per_chunk, int ksplit, float ts, float *__restrict__ C,
-    float *__restrict__ part, unsigned *__restrict__ counters) {
-  extern __shared__ __align__(16) uint16_t lds[];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int h = lane >> 4, col = lane & 15;
+__device__ inline void compute_wtile(const WTile &t, const bf16x8 (&b)[MB][8], f32x4 (&acc)[MB]) {
+  float s[4];
+  scales4(t.s, s);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t cw[4] = {t.c[c].x, t.c[c].y, t.c[c].z, t.c[c].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 wf = dequant8(cw[j], s[2 * c + (j >> 1)]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, b[mb][4 * c + j], acc[mb], 0, 0, 0);
+    }
+  }
+}
+
+// Occupancy target (waves per SIMD) for the register allocator.
+template <int MB, int R>
+constexpr int waves_per_simd() {
+  return MB == 1 ? 3 : 2;
+}
+
+// ABUF = 2 double-buffers the activation fragments; with ABUF = 1 the next
+// k-tile's fragments are loaded after the last use of the current ones (large
+// M, where two copies do not fit in registers).
+template <int MB, int R, int ABUF>
+__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MB, R>())))
+void k_gemm(const uint8_t *__restrict__ act, int M, int act_bytes, const uint8_t *__restrict__ W,
+            int N, int nrt, int nkt, int kts_per_split, int ksplit, float ts,
+            float *__restrict__ C, float *__restrict__ part, unsigned *__restrict__ counters) {
+  extern __shared__ __align__(16) f32x4 red[];  // [WG_WAVES][R][MB][64]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int rb = blockIdx.x, ks = blockIdx.y;
-  const int kt0 = ks * kts_per_split;
-  const int kt1 = min(nkt, kt0 + kts_per_split);
-  const int rt = rb * WG_WAVES + wave;
-  const bool active = rt < nrt;
-  const uint8_t *stripe = W + (size_t)(active ? rt : 0) * (size_t)nkt * TILE_BYTES;
+  const int rt0 = rb * R;
+  const int kA = ks * kts_per_split;
+  const int kB = min(nkt, kA + kts_per_split);
+  const int len = kB - kA;
+  const int kbeg = kA + (len * wave) / WG_WAVES;
+  const int n = kA + (len * (wave + 1)) / WG_WAVES - kbeg;  // k-tiles of this wave
+  const int stripe_bytes = nkt * TILE_BYTES;
 
-  f32x4 acc[MB];
+  // One buffer resource per row tile (a row tile past the matrix has no
+  // records, so its loads return zeros), one for the packed activations.
+  __amdgpu_buffer_rsrc_t rs[R];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < R; ++r) {
+    const int rt = rt0 + r;
+    const uint8_t *base = W + (size_t)min(rt, nrt - 1) * (size_t)stripe_bytes;
+    rs[r] = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, rt < nrt ? stripe_bytes : 0,
+                                              RAW_BUFFER_FLAGS);
+  }
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void *)act, (short)0, act_bytes, RAW_BUFFER_FLAGS);
 
-  for (int c0 = kt0; c0 < kt1; c0 += kts_per_chunk) {
-    const int c1 = min(kt1, c0 + kts_per_chunk);
-    const int kspan = (c1 - c0) * K_PER_TILE;
-    const int pitch = kspan + 8;  // bf16 elements; 16-byte pad staggers LDS banks
-    // Stage A[0..M)[c0*128 .. c0*128 + kspan) (zeros beyond K).
-    const int cpr = kspan / 8;  // 16-byte chunks per row
-    __syncthreads();            // previous chunk fully consumed
-    for (int c = tid; c < M * cpr; c += WG_THREADS) {
-      const int m = c / cpr, kc = c - m * cpr;
-      const int kg = c0 * K_PER_TILE + kc * 8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (kg < K) v = *reinterpret_cast<const uint4 *>(A + (size_t)m * K + kg);
-      *reinterpret_cast<uint4 *>(lds + m * pitch + kc * 8) = v;
-    }
-    __syncthreads();
-    if (active) {
-      for (int kt = c0; kt < c1; ++kt) {
-        const int g = kt >> 3, t = kt & 7;
-        const int q = min(TILES_PER_GROUP, nkt - g * TILES_PER_GROUP);
-        const uint8_t *grp = stripe + (size_t)g * TILES_PER_GROUP * TILE_BYTES;
-        const uint4 cw = *reinterpret_cast<const uint4 *>(grp + t * CODE_TILE_BYTES + lane * 16);
-        const uint32_t sc =
-            *reinterpret_cast<const uint16_t *>(grp + q * CODE_TILE_BYTES + lane * 2 * q + 2 * t);
-        const float s0 = e4m3_to_f32(sc & 0xFFu), s1 = e4m3_to_f32(sc >> 8);
-        const bf16x8 w0 = dequant8(cw.x, s0), w1 = dequant8(cw.y, s0);
-        const bf16x8 w2 = dequant8(cw.z, s1), w3 = dequant8(cw.w, s1);
-        const int kl = (kt - c0) * K_PER_TILE + 32 * h;
+  f32x4 acc[R][MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int m = mb * 16 + col;
-          bf16x8 b0, b1, b2, b3;
-          if (m < M) {
-            const uint16_t *ap = lds + m * pitch + kl;
-            b0 = lds_b(ap);
-            b1 = lds_b(ap + 8);
-            b2 = lds_b(ap + 16);
-            b3 = lds_b(ap + 24);
-          } else {
-            b0 = b1 = b2 = b3 = bf16x8{};
-          }
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, b0, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, b1, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2, b2, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w3, b3, acc[mb], 0, 0, 0);
-        }
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[r][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  WTile w[R];
+  bf16x8 a0[MB][8];
+  load_afrag<MB>(a0, ra, kbeg, n > 0, M, lane);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_wtile(w[r], rs[r], kbeg, n > 0, lane);
+  if constexpr (ABUF == 2) {
+    bf16x8 a1[MB][8];
+    load_afrag<MB>(a1, ra, kbeg + 1, n > 1, M, lane);
+    for (int i = 0; i < n; i += 2) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        compute_wtile<MB>(w[r], a0, acc[r]);
+        load_wtile(w[r], rs[r], kbeg + i + 1, i + 1 < n, lane);
       }
+      load_afrag<MB>(a0, ra, kbeg + i + 2, i + 2 < n, M, lane);
+      if (i + 1 >= n) break;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        compute_wtile<MB>(w[r], a1, acc[r]);
+        load_wtile(w[r], rs[r], kbeg + i + 2, i + 2 < n, lane);
+      }
+      load_afrag<MB>(a1, ra, kbeg + i + 3, i + 3 < n, M, lane);
+    }
+  } else {
+    for (int i = 0; i < n; ++i) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        compute_wtile<MB>(w[r], a0, acc[r]);
+        load_wtile(w[r], rs[r], kbeg + i + 1, i + 1 < n, lane);
+      }
+      load_afrag<MB>(a0, ra, kbeg + i + 1, i + 1 < n, M, lane);
     }
   }
 
-  // Lane (h, col) holds D[n = 16 rt + 4h + i][m = 16 mb + col], i = 0..3.
+  // Sum the 4 waves' tiles in wave order.
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
+  __syncthreads();
+
   const int npad = nrt * ROWS_PER_TILE;
-  const int n0 = rt * ROWS_PER_TILE + 4 * h;
-  if (ksplit == 1) {
-    if (active) {
+  constexpr int ITEMS = R * MB * 64;
+  for (int it = tid; it < ITEMS; it += WG_THREADS) {
+    const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+    f32x4 v = red[((0 * R + r) * MB + mb) * 64 + l];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int m = mb * 16 + col;
-        if (m >= M) continue;
-        float *dst = C + (size_t)m * N + n0;
-        if ((N & 3) == 0) {
-          if (n0 < N) *reinterpret_cast<f32x4 *>(dst) = acc[mb] * ts;
-        } else {
-          for (int i = 0; i < 4; ++i)
-            if (n0 + i < N) dst[i] = acc[mb][i] * ts;
-        }
+    for (int wv = 1; wv < WG_WAVES; ++wv) v += red[((wv * R + r) * MB + mb) * 64 + l];
+    // lane l of a tile holds D[n = 16 rt + 4 (l / 16) + i][m = 16 mb + l % 16]
+    const int m = mb * 16 + (l & 15);
+    const int rt = rt0 + r;
+    const int n0 = rt * ROWS_PER_TILE + 4 * (l >> 4);
+    if (m >= M || rt >= nrt) continue;
+    if (ksplit == 1) {
+      float *dst = C + (size_t)m * N + n0;
+      if ((N & 3) == 0) {
+        if (n0 < N) *reinterpret_cast<f32x4 *>(dst) = v * ts;
+      } else {
+        for (int i = 0; i < 4; ++i)
+          if (n0 + i < N) dst[i] = v[i] * ts;
       }
-    }
-    return;
-  }
-
-  if (active) {
+    } else {
+      float *dst = part + ((size_t)ks * M + m) * npad + n0;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = mb * 16 + col;
-      if (m < M) *reinterpret_cast<f32x4 *>(part + ((size_t)ks * M + m) * npad + n0) = acc[mb];
+      for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(dst + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
-  __threadfence();
+  if (ksplit == 1) return;
+
+  // The partial stores have reached memory once this wave's counters drain.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   __shared__ unsigned s_ticket;
-  if (tid == 0) s_ticket = atomicAdd(&counters[rb], 1u);
+  if (tid == 0)
+    s_ticket = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   __syncthreads();
   if (s_ticket != (unsigned)(ksplit - 1)) return;
-  __threadfence();
-  const int rows = WG_WAVES * ROWS_PER_TILE;
+  const int rows = R * ROWS_PER_TILE;
   for (int e = tid; e < M * rows; e += WG_THREADS) {
-    const int m = e / rows, n = rb * rows + (e - m * rows);
-    if (n >= N) continue;
-    float sum = 0.f;
-    for (int s = 0; s < ksplit; ++s) sum += part[((size_t)s * M + m) * npad + n];
-    C[(size_t)m * N + n] = sum * ts;
+    const int m = e / rows, nn = rt0 * ROWS_PER_TILE + (e - m * rows);
+    if (nn >= N) continue;
+    float sum = __hip_atomic_load(part + (size_t)m * npad + nn, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_SYSTEM);
+    for (int s2 = 1; s2 < ksplit; ++s2)
+      sum += __hip_atomic_load(part + ((size_t)s2 * M + m) * npad + nn, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+    C[(size_t)m * N + nn] = sum * ts;
   }
-  if (tid == 0) counters[rb] = 0u;  // ready for the next launch
+  if (tid == 0) __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+typedef void (*GemmKernel)(const uint8_t *, int, int, const uint8_t *, int, int, int, int, int,
+                           float, float *, float *, unsigned *);
+
+GemmKernel pick_kernel(int mb, int r) {
+  switch (mb * 8 + r) {
+    case 1 * 8 + 2: return k_gemm<1, 2, 2>;
+    case 1 * 8 + 4: return k_gemm<1, 4, 2>;
+    case 2 * 8 + 2: return k_gemm<2, 2, 2>;
+    case 2 * 8 + 4: return k_gemm<2, 4, 2>;
+    case 3 * 8 + 2: return k_gemm<3, 2, 1>;
+    case 3 * 8 + 4: return k_gemm<3, 4, 1>;
+    case 4 * 8 + 2: return k_gemm<4, 2, 1>;
+    case 4 * 8 + 4: return k_gemm<4, 4, 1>;
+    default: return nullptr;
+  }
+}
+
+// Row-major A -> packed activations: one thread per 16-byte chunk.
+__global__ void k_pack_act(const uint16_t *__restrict__ A, int M, int K, int mblocks, int nkt,
+                           uint4 *__restrict__ out) {
+  const int64_t total = (int64_t)nkt * mblocks * 8 * 64;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int lane = (int)(idx & 63);
+  const int64_t frag = idx >> 6;  // (kt * MB + mb) * 8 + q
+  const int q = (int)(frag & 7);
+  const int64_t kt_mb = frag >> 3;
+  const int mb = (int)(kt_mb % mblocks);
+  const int64_t kt = kt_mb / mblocks;
+  const int row = mb * 16 + (lane & 15);
+  const int64_t k0 = kt * K_PER_TILE + 64 * (lane >> 4) + 8 * q;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < M && k0 < K) v = *reinterpret_cast<const uint4 *>(A + (size_t)row * K + k0);
+  out[idx] = v;
 }
 
 }  // namespace
 
 namespace nvfp4v {
 
+// Tile table: R (row tiles per work-group, sharing one activation fragment),
+// then enough work-groups along K that about 1.5 work-groups per CU exist,
+// keeping at least 2 k-tiles per wave.
 int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
-  p->variant = 0;
   p->mblocks = (int)((m + 15) / 16);
+  p->rb = 4;
   p->waves = WG_WAVES;
-  p->row_tiles_per_wg = WG_WAVES;
-  p->grid_x = (int)((L.nrt + WG_WAVES - 1) / WG_WAVES);
+  p->grid_x = (int)((L.nrt + p->rb - 1) / p->rb);
   const int nkt = (int)L.nkt;
-  // k-tiles per LDS chunk for this M
-  const int per_row = LDS_BUDGET / (2 * (int)m);
-  int chunk = (per_row - 8) / K_PER_TILE;
-  chunk = std::max(1, std::min(chunk, nkt));
-  // split K so that about 4 work-groups per CU are in flight
-  const int target = 4 * std::max(1, ctx->num_cus);
+  const int target = std::max(1, (3 * std::max(1, ctx->num_cus)) / 2);
   int ks = std::max(1, (target + p->grid_x - 1) / p->grid_x);
-  ks = std::min(ks, nkt);
+  ks = std::min(ks, std::max(1, nkt / (2 * WG_WAVES)));
   int per = (nkt + ks - 1) / ks;
   ks = (nkt + per - 1) / per;
   p->ksplit = ks;
   p->ktiles_per_split = per;
   p->grid_y = ks;
-  // an LDS chunk never spans more than the split
-  p->ktiles_per_chunk = std::min(chunk, per);
-  p->lds_bytes = (size_t)m * (size_t)(p->ktiles_per_chunk * K_PER_TILE + 8) * 2;
+  p->lds_bytes = (size_t)WG_WAVES * p->rb * p->mblocks * 64 * sizeof(f32x4);
   return NVFP4V_OK;
 }
 
+int launch_pack_act(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
+                    hipStream_t stream) {
+  const int mb = (int)((m + 15) / 16), nkt = (int)((k + 255) / 256);
+  const int64_t total = (int64_t)nkt * mb * 8 * 64;
+  hipLaunchKernelGGL(k_pack_act, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, a,
+                     (int)m, (int)k, mb, nkt, (uint4 *)act);
+  return hip_status(ctx, hipGetLastError());
+}
+
+int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
+                int64_t n, float ts, float *c, hipStream_t stream) {
+  Layout L;
+  if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
+  Plan p;
+  int rc = make_plan(ctx, L, m, &p);
+  if (rc) return rc;
+  if (p.ksplit > 1) {
+    const size_t need = (size_t)p.ksplit * (size_t)m * (size_t)(L.nrt * ROWS_PER_TILE);
+    if (need > ctx->partial_floats || (size_t)p.grid_x > ctx->n_counters) return NVFP4V_E_WORKSPACE;
+  }
+  GemmKernel kern = pick_kernel(p.mblocks, p.rb);
+  if (!kern) return NVFP4V_E_INVALID_ARG;
+  if (fault_injected()) return NVFP4V_E_FAULT;
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.grid_x, (unsigned)p.grid_y), dim3(WG_THREADS),
+                     p.lds_bytes, stream, act, (int)m, (int)act_packed_bytes(m, k),
+                     (const uint8_t *)packed, (int)n, (int)L.nrt, (int)L.nkt, p.ktiles_per_split,
+                     p.ksplit, ts, c, ctx->partials, ctx->counters);
+  return hip_status(ctx, hipGetLastError());
+}
+
 }  // namespace nvfp4v
+
+extern "C" size_t nvfp4v_act_packed_bytes(int64_t m, int64_t k) {
+  if (m < 1 || m > NVFP4V_MAX_M || k < 16 || k % 16 != 0 || k > (int64_t(1) << 22)) return 0;
+  return act_packed_bytes(m, k);
+}
+
+extern "C" int nvfp4v_pack_activations(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k,
+                                       void *act, hipStream_t stream) {
+  if (!ctx || !a || !act) return NVFP4V_E_INVALID_ARG;
+  if (m < 1 || m > NVFP4V_MAX_M) return NVFP4V_E_M_RANGE;
+  if (k < 16 || k % 16 != 0 || k > (int64_t(1) << 22)) return NVFP4V_E_SHAPE;
+  if (!aligned16(a) || !aligned16(act)) return NVFP4V_E_ALIGN;
+  if (fault_injected()) return NVFP4V_E_FAULT;
+  return launch_pack_act(ctx, a, m, k, (uint8_t *)act, stream);
+}
+
+extern "C" int nvfp4v_verify_gemm_pa(nvfp4v_ctx *ctx, const void *act, int64_t m, int64_t k,
+                                     const void *packed, int64_t n, float ts, float *c,
+                                     hipStream_t stream) {
+  if (!ctx || !act || !packed || !c) return NVFP4V_E_INVALID_ARG;
+  if (m < 1 || m > NVFP4V_MAX_M) return NVFP4V_E_M_RANGE;
+  Layout L;
+  if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
+  if (!aligned16(act) || !aligned16(packed) || !aligned16(c)) return NVFP4V_E_ALIGN;
+  return launch_gemm(ctx, (const uint8_t *)act, m, k, packed, n, ts, c, stream);
+}
 
 extern "C" int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k,
                                   const void *packed, int64_t n, float ts, float *c,
@@ -230,6 +395,7 @@ extern "C" int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m,
   Layout L;
   if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
   if (!aligned16(a) || !aligned16(packed) || !aligned16(c)) return NVFP4V_E_ALIGN;
+  if (act_packed_bytes(m, k) > ctx->act_bytes) return NVFP4V_E_WORKSPACE;
   Plan p;
   int rc = make_plan(ctx, L, m, &p);
   if (rc) return rc;
@@ -238,20 +404,9 @@ extern "C" int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m,
     if (need > ctx->partial_floats || (size_t)p.grid_x > ctx->n_counters) return NVFP4V_E_WORKSPACE;
   }
   if (fault_injected()) return NVFP4V_E_FAULT;
-  const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y);
-  const dim3 block(WG_THREADS);
-#define LAUNCH(MBV)                                                                               \
-  hipLaunchKernelGGL(k_gemm_mfma<MBV>, grid, block, p.lds_bytes, stream, a, (int)m, (int)k,      \
-                     (const uint8_t *)packed, (int)n, (int)L.nrt, (int)L.nkt, p.ktiles_per_split, \
-                     p.ktiles_per_chunk, p.ksplit, ts, c, ctx->partials, ctx->counters)
-  switch (p.mblocks) {
-    case 1: LAUNCH(1); break;
-    case 2: LAUNCH(2); break;
-    case 3: LAUNCH(3); break;
-    default: LAUNCH(4); break;
-  }
-#undef LAUNCH
-  return hip_status(ctx, hipGetLastError());
+  rc = launch_pack_act(ctx, a, m, k, ctx->act, stream);
+  if (rc) return rc;
+  return launch_gemm(ctx, ctx->act, m, k, packed, n, ts, c, stream);
 }
 
 extern "C" int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64_t m, char *buf,
@@ -263,8 +418,7 @@ extern "C" int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64
   Plan p;
   int rc = make_plan(ctx, L, m, &p);
   if (rc) return rc;
-  snprintf(buf, len, "mfma16x16x32 mblocks=%d waves=%d rows/wg=%d grid=%dx%d ksplit=%d kt/split=%d kt/chunk=%d lds=%zu",
-           p.mblocks, p.waves, p.row_tiles_per_wg * ROWS_PER_TILE, p.grid_x, p.grid_y, p.ksplit,
-           p.ktiles_per_split, p.ktiles_per_chunk, p.lds_bytes);
+  snprintf(buf, len, "mfma16x16x32 mblocks=%d r=%d waves=%d grid=%dx%d ksplit=%d kt/split=%d lds=%zu",
+           p.mblocks, p.rb, p.waves, p.grid_x, p.grid_y, p.ksplit, p.ktiles_per_split, p.lds_bytes);
   return NVFP4V_OK;
 }

@@ -12,34 +12,30 @@
 // ---------------------------------------------------------------------------
 // Packed (device) layout.
 //
-// The weight matrix is cut into row tiles of 16 rows. Each row tile is one
-// contiguous stripe covering all of K, cut into k-tiles of 128 elements, and
-// the k-tiles are grouped in super-groups of up to 8:
+// The weight matrix is cut into row tiles of 16 rows; each row tile is one
+// contiguous stripe over all of K, cut into k-tiles of 256 elements:
 //
-//   stripe(rt)      = rt * nkt * TILE_BYTES
-//   super-group g   = stripe + g * 8 * TILE_BYTES, holding q = min(8, nkt - 8g)
-//                     k-tiles as [q x 1024 code bytes][q x 128 scale bytes]
-//   code tile t     : 1024 bytes; lane L = r + 16h (r = row in tile, h = 0..3)
-//                     owns bytes [16L, 16L + 16) = the 32 codes of row r for
-//                     k in [128 kt + 32h, 128 kt + 32h + 32), canonical order
-//                     (byte b: low nibble k = 2b, high nibble 2b + 1)
-//   scale block     : lane L owns bytes [2qL, 2qL + 2q); byte 2t + e is the
-//                     E4M3 scale of row r, 16-block 8 kt + 2h + e (kt = 8g + t)
+//   tile(rt, kt)  = (rt * nkt + kt) * TILE_BYTES            (2304 bytes)
+//   code half c   : bytes [1024 c, 1024 c + 1024), c = 0, 1; lane L = r + 16h
+//                   (r = row in tile, h = 0..3) owns 16 bytes at 16 L: the 32
+//                   codes of row r for k in [256 kt + 64 h + 32 c, +32), in
+//                   canonical order (byte b: low nibble k = 2b, high 2b + 1)
+//   scales        : bytes [2048 + 4 L, 2048 + 4 L + 4): byte e is the E4M3
+//                   scale of row r, 16-block 16 kt + 4 h + e
 //
-// One wave reads a code tile with one 16-byte load per lane (1 KiB fully
-// contiguous per wave), and the lane's 32 codes are exactly what it feeds to
-// four 16x16x32 MFMAs (8 consecutive k per MFMA). Each byte of the canonical
-// format appears once; padding (rows >= N, k >= K) is zero codes / zero
-// scales, so it contributes exact zeros.
+// A wave reads a tile with three fully coalesced loads (2 x 1 KiB of codes,
+// 256 bytes of scales). Dword j of code half c holds the 8 codes the lane
+// feeds to MFMA (c, j) of the tile, and its scale is byte 2c + j/2. Each byte
+// of the canonical format appears once; padding (rows >= N, k >= K) is zero
+// codes with zero scales, which contributes exact zeros.
 // ---------------------------------------------------------------------------
 namespace nvfp4v {
 
 constexpr int ROWS_PER_TILE = 16;
-constexpr int K_PER_TILE = 128;
-constexpr int CODE_TILE_BYTES = 1024;
-constexpr int SCALE_TILE_BYTES = 128;
-constexpr int TILE_BYTES = CODE_TILE_BYTES + SCALE_TILE_BYTES;  // 1152
-constexpr int TILES_PER_GROUP = 8;
+constexpr int K_PER_TILE = 256;
+constexpr int CODE_HALF_BYTES = 1024;
+constexpr int SCALE_OFFSET = 2048;
+constexpr int TILE_BYTES = 2304;
 
 struct Layout {
   int64_t n, k;
@@ -48,9 +44,30 @@ struct Layout {
   size_t bytes() const { return (size_t)nrt * (size_t)nkt * TILE_BYTES; }
 };
 
+// Activations in MFMA fragment order ("packed activations"): for k-tile kt,
+// 16-row block mb and fragment q = 0..7, a 1 KiB chunk at
+//   ((kt * MB + mb) * 8 + q) * 1024
+// whose lane L = col + 16 h holds 8 bf16: A[16 mb + col][256 kt + 64 h + 8 q + e],
+// e = 0..7 (MB = ceil(M / 16)). A wave reads one fragment with one fully
+// coalesced 16-byte load per lane. Rows >= M are never read.
+constexpr int ACT_FRAG_BYTES = 1024;
+
+inline size_t act_packed_bytes(int64_t m, int64_t k) {
+  const int64_t mb = (m + 15) / 16, nkt = (k + 255) / 256;
+  return (size_t)nkt * (size_t)mb * 8 * ACT_FRAG_BYTES;
+}
+
+// Byte offset of element (row, col) of A inside the packed activations.
+__host__ __device__ inline size_t act_offset(int64_t row, int64_t k, int mblocks) {
+  const int64_t kt = k >> 8, rem = k & 255;
+  const int64_t h = rem >> 6, q = (rem >> 3) & 7, e = rem & 7;
+  const int64_t mb = row >> 4, col = row & 15;
+  return (size_t)(((kt * mblocks + mb) * 8 + q) * ACT_FRAG_BYTES + (col + 16 * h) * 16 + 2 * e);
+}
+
 inline bool make_layout(int64_t n, int64_t k, Layout *L) {
   if (n < 1 || k < 16 || k % 16 != 0) return false;
-  if (n > (int64_t(1) << 31) || k > (int64_t(1) << 24)) return false;
+  if (n > (int64_t(1) << 31) || k > (int64_t(1) << 22)) return false;  // keeps 32-bit buffer offsets in range
   L->n = n;
   L->k = k;
   L->nrt = (n + ROWS_PER_TILE - 1) / ROWS_PER_TILE;
@@ -145,15 +162,13 @@ __host__ __device__ inline uint32_t quantize_block(const float *w, uint8_t *code
 // Context.
 // ---------------------------------------------------------------------------
 struct Plan {
-  int variant;      // 0 = MFMA bf16
-  int mblocks;      // ceil(M / 16)
-  int waves;        // waves per work-group
-  int row_tiles_per_wg;
-  int ksplit;       // work-groups along K
-  int ktiles_per_split;
-  int ktiles_per_chunk;  // k-tiles of activations staged in LDS at a time
-  int grid_x, grid_y;
-  size_t lds_bytes;
+  int mblocks;           // ceil(M / 16): 16-column MFMA blocks of activations
+  int rb;                // row tiles per work-group (every wave of it covers all of them)
+  int waves;             // waves per work-group; they split the group's k-range
+  int ksplit;            // work-groups along K (fixed-order reduction when > 1)
+  int ktiles_per_split;  // k-tiles per work-group
+  int grid_x, grid_y;    // row blocks, k splits
+  size_t lds_bytes;      // cross-wave reduction buffer
 };
 
 }  // namespace nvfp4v
@@ -166,6 +181,8 @@ struct nvfp4v_ctx {
   size_t partial_floats = 0;
   unsigned *counters = nullptr;  // per row-block arrival counters (kept at 0 between calls)
   size_t n_counters = 0;
+  uint8_t *act = nullptr;  // packed activations for nvfp4v_verify_gemm
+  size_t act_bytes = 0;
 };
 
 namespace nvfp4v {
@@ -173,4 +190,10 @@ int fault_injected();  // NVFP4V_FAULT=launch
 int hip_status(nvfp4v_ctx *ctx, hipError_t e);
 bool aligned16(const void *p);
 int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p);
+// Enqueue A (row-major bf16) -> packed activations (no argument checks).
+int launch_pack_act(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
+                    hipStream_t stream);
+// Enqueue the GEMM on packed activations (no argument checks).
+int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
+                int64_t n, float ts, float *c, hipStream_t stream);
 }  // namespace nvfp4v

@@ -30,14 +30,10 @@ __global__ void k_fill_packed(uint8_t *buf, size_t copy_stride, int copies, int6
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
     const size_t c = i / per, off = i - c * per;
-    const size_t stripe = (size_t)nkt * TILE_BYTES;
-    const size_t in_stripe = off % stripe;
-    const size_t g = in_stripe / ((size_t)TILES_PER_GROUP * TILE_BYTES);
-    const size_t in_group = in_stripe - g * (size_t)TILES_PER_GROUP * TILE_BYTES;
-    const int64_t q = std::min<int64_t>(TILES_PER_GROUP, nkt - (int64_t)g * TILES_PER_GROUP);
+    const size_t in_tile = off % TILE_BYTES;
     const uint32_t r = mix32(seed ^ (i * 0x9E3779B97F4A7C15ULL));
     uint8_t v = (uint8_t)r;
-    if (in_group >= (size_t)q * CODE_TILE_BYTES) v = (uint8_t)(0x20 + (r % 0x21));
+    if (in_tile >= (size_t)SCALE_OFFSET) v = (uint8_t)(0x20 + (r % 0x21));
     buf[c * copy_stride + off] = v;
   }
 }

@@ -70,8 +70,8 @@ def _load():
     lib.oracle_bf16_from_f32.restype = None
     lib.oracle_glue_scale.argtypes = [p, i64, c.c_float, p]
     lib.oracle_glue_scale.restype = None
-    lib.oracle_glue_mul.argtypes = [p, p, i64, c.c_float, p]
-    lib.oracle_glue_mul.restype = None
+    lib.oracle_glue_sum.argtypes = [p, p, i64, c.c_float, p]
+    lib.oracle_glue_sum.restype = None
     _lib = lib
     return lib
 
@@ -178,14 +178,14 @@ def glue_scale(x: np.ndarray, cst: float) -> np.ndarray:
     return out
 
 
-def glue_mul(x: np.ndarray, y: np.ndarray, cst: float) -> np.ndarray:
-    """bf16((x * c) * (y * c)) elementwise, fp32 throughout."""
+def glue_sum(x: np.ndarray, y: np.ndarray, cst: float) -> np.ndarray:
+    """bf16(x * c + y * c) elementwise: two fp32 products, one fp32 sum (no FMA)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     y = np.ascontiguousarray(y, dtype=np.float32)
     if x.shape != y.shape:
         raise ValueError("shape mismatch")
     out = np.empty(x.shape, np.uint16)
-    _load().oracle_glue_mul(_ptr(x), _ptr(y), x.size, float(np.float32(cst)), _ptr(out))
+    _load().oracle_glue_sum(_ptr(x), _ptr(y), x.size, float(np.float32(cst)), _ptr(out))
     return out
 
 

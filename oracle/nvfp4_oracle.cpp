@@ -299,12 +299,13 @@ void oracle_glue_scale(const float *x, int64_t count, float cst, uint16_t *out) 
   }
 }
 
-//   out = bf16( (x * c) * (y * c) )          (three fp32 products, then RNE)
-void oracle_glue_mul(const float *x, const float *y, int64_t count, float cst, uint16_t *out) {
+//   out = bf16( x * c + y * c )              (two fp32 products and one fp32
+//                                             sum, no fused multiply-add, then RNE)
+void oracle_glue_sum(const float *x, const float *y, int64_t count, float cst, uint16_t *out) {
   for (int64_t i = 0; i < count; ++i) {
     volatile float px = x[i] * cst;
     volatile float py = y[i] * cst;
-    volatile float p = px * py;
+    volatile float p = px + py;
     out[i] = bf16_from_float_rne(p);
   }
 }

@@ -35,7 +35,7 @@ def test_packed_bytes():
     assert nv.packed_bytes(5120, 17408) == 50135040
     assert nv.packed_bytes(151936, 5120) == 437575680
     assert nv.packed_bytes(512, 256) == 73728
-    assert nv.packed_bytes(17, 48) == 2 * 1 * 1152   # padded to 32 rows x 128 k
+    assert nv.packed_bytes(17, 48) == 2 * 1 * 2304   # padded to 32 rows x 256 k
     assert nv.packed_bytes(0, 256) == 0
     assert nv.packed_bytes(16, 40) == 0
 

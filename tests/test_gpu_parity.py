@@ -236,3 +236,19 @@ def test_row_invariance(torch_cuda, ctx, oracle_mod):
 def test_staircase_runs(ctx):
     us = ctx.staircase(512, 256, 1, 4, warmup=1, reps=3, rotate_bytes=0)
     assert us.shape == (4,) and (us > 0).all()
+
+
+def test_prepacked_activations_match(torch_cuda, ctx):
+    """verify_gemm_pa on pack_activations output equals verify_gemm, bitwise."""
+    torch = torch_cuda
+    g = np.random.default_rng(21)
+    for (n, k) in [(100, 144), (512, 5120), (64, 1040)]:
+        codes, scales = random_codes_scales(g, n, k)
+        packed = pack_dev(torch, ctx, codes, scales, n, k)
+        a = bf16_dev(torch, synth.activations_bf16(64, k, seed=5, outliers=True))
+        for m in (1, 7, 16, 40, 64):
+            ref = ctx.verify_gemm(a[:m], packed, n, k)
+            act = ctx.pack_activations(a[:m].contiguous())
+            assert act.numel() == nv.act_packed_bytes(m, k)
+            got = ctx.verify_gemm_pa(act, m, k, packed, n)
+            assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), (n, k, m)

@@ -1,0 +1,179 @@
+"""The chained verify pass on the GPU.
+
+Only layer 0's GEMMs see inputs drawn by the generator, so the oracle checks
+those directly. Deeper layers are checked by properties that hold at any size:
+- the pass equals the composition of single verify_gemm / glue calls, bitwise;
+- graph replays equal the eager pass, bitwise;
+- every glue kernel equals the oracle's glue, bitwise, on generator inputs;
+- activations stay finite with an O(1) RMS through the 64-layer stack.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import nvfp4_skinny_gemm_amd as nv
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+@pytest.fixture(scope="module")
+def ctx(torch_cuda):
+    c = nv.Context(0)
+    yield c
+    c.close()
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+def test_glue_kernels_match_oracle(torch_cuda, ctx, oracle_mod):
+    torch = torch_cuda
+    g = np.random.default_rng(11)
+    x = (g.standard_normal((16, 3 * 512)) * 40).astype(np.float32)
+    y = (g.standard_normal((16, 3 * 512)) * 40).astype(np.float32)
+    xd, yd = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
+    c = f32(1 / math.sqrt(5120))
+    got = ctx.glue_scale(xd[:, 1024:], c).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, oracle_mod.glue_scale(x[:, 1024:], c))
+    c2 = f32(1 / math.sqrt(2 * 5120))
+    got = ctx.glue_sum(xd[:, :512], yd[:, 512:1024], c2).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, oracle_mod.glue_sum(x[:, :512], y[:, 512:1024], c2))
+
+
+def small_stack(torch, ctx, layers, H, I, seed=0):
+    packed = []
+    for l in range(layers):
+        mats = {}
+        for name, parts, n, k in (("qkv", ("q", "k", "v"), 3 * H, H), ("o", ("o",), H, H),
+                                  ("gate_up", ("gate", "up"), 2 * I, H), ("down", ("down",), H, I)):
+            w = torch.cat([synth.weights_f32_cuda(n // len(parts), k, seed=seed,
+                                                  stream="t%d/%s" % (l, p)) for p in parts])
+            codes, scales = ctx.quantize(w)
+            mats[name] = ctx.pack(codes, scales, n, k)
+        packed.append(mats)
+    arr = (nv.Layer * layers)()
+    for l, m in enumerate(packed):
+        arr[l] = nv.Layer(m["qkv"].data_ptr(), m["o"].data_ptr(), m["gate_up"].data_ptr(),
+                          m["down"].data_ptr(), 1.0, 1.0, 1.0, 1.0)
+    return packed, arr
+
+
+def manual_chain(torch, ctx, packed, h0, H, I):
+    c_h, c_i, c_2 = f32(1 / math.sqrt(H)), f32(1 / math.sqrt(I)), f32(1 / math.sqrt(2 * H))
+    h = h0
+    outs = []
+    for mats in packed:
+        qkv = ctx.verify_gemm(h, mats["qkv"], 3 * H, H)
+        o = ctx.verify_gemm(ctx.glue_scale(qkv[:, 2 * H:], c_h), mats["o"], H, H)
+        gu = ctx.verify_gemm(ctx.glue_scale(o, c_h), mats["gate_up"], 2 * I, H)
+        d = ctx.verify_gemm(ctx.glue_sum(gu[:, :I], gu[:, I:], c_2), mats["down"], H, I)
+        h = ctx.glue_scale(d, c_i)
+        outs.append(h)
+    return outs
+
+
+@pytest.mark.parametrize("m", [1, 8, 16, 33, 64])
+def test_pass_equals_composition(torch_cuda, ctx, m):
+    torch = torch_cuda
+    H, I, L = 256, 512, 3
+    packed, arr = small_stack(torch, ctx, L, H, I)
+    h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=3).view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I), dtype=torch.uint8, device="cuda")
+    h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    trace = torch.empty((L, m, H), dtype=torch.bfloat16, device="cuda")
+    ctx.verify_pass(arr, H, I, h0[:m], ws, h_out, trace=trace)
+    ref = manual_chain(torch, ctx, packed, h0[:m], H, I)
+    for l in range(L):
+        assert torch.equal(trace[l].view(torch.int16), ref[l].view(torch.int16)), "layer %d" % l
+    assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16))
+
+
+def test_graph_replays_equal_eager(torch_cuda, ctx):
+    torch = torch_cuda
+    H, I, L, m = 512, 1024, 4, 16
+    packed, arr = small_stack(torch, ctx, L, H, I, seed=1)
+    h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=4).view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I), dtype=torch.uint8, device="cuda")
+    eager = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    ctx.verify_pass(arr, H, I, h0[:m], ws, eager)
+    torch.cuda.synchronize()
+    out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ctx.verify_pass(arr, H, I, h0[:m], ws, out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ctx.verify_pass(arr, H, I, h0[:m], ws, out)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), "replay %d" % rep
+        # unrelated eager work between replays
+        ctx.verify_gemm(h0[:m], packed[0]["qkv"], 3 * H, H)
+        torch.cuda.synchronize()
+
+
+def test_full_size_layer0_against_oracle(torch_cuda, ctx, oracle_mod):
+    """One layer of the full-size stack through the pass (M = 16): its q|k|v outputs,
+    whose input comes from the generator, are checked against the oracle on 1536
+    sampled weight rows."""
+    torch = torch_cuda
+    H, I, m = 5120, 17408, 16
+    log("full-size layer 0")
+    packed, arr = small_stack(torch, ctx, 1, H, I, seed=2)
+    a = synth.activations_bf16(64, H, seed=0, stream="pass/h0")
+    h0 = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I), dtype=torch.uint8, device="cuda")
+    h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    ctx.verify_pass(arr, H, I, h0[:m], ws, h_out)
+    torch.cuda.synchronize()
+    qkv = ws[: m * 3 * H * 4].view(torch.float32).view(m, 3 * H).cpu().numpy()
+    rows = np.sort(np.random.default_rng(5).choice(3 * H, 1536, replace=False))
+    w = torch.cat([synth.weights_f32_cuda(H, H, seed=2, stream="t0/%s" % p) for p in ("q", "k", "v")])
+    w_rows = w[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del w
+    oc, osc = oracle_mod.quantize(w_rows)
+    c_ref, s_ref = oracle_mod.gemm(a[:m], oc, osc)
+    ok = oracle_mod.within_tolerance(qkv[:, rows], c_ref, s_ref)
+    assert ok.all(), "%d of %d sampled qkv outputs outside 1e-5*S" % ((~ok).sum(), ok.size)
+
+
+def test_full_stack_stays_finite_and_bounded(torch_cuda, ctx):
+    """64 layers at full size, M = 16: the linear glue keeps the RMS O(1)."""
+    torch = torch_cuda
+    H, I, L, m = 5120, 17408, 64, 16
+    log("building 64-layer stack")
+    packed, arr = small_stack(torch, ctx, L, H, I, seed=7)
+    h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=0, stream="pass/h0").view(np.int16)).cuda()
+    h0 = h0.view(torch.bfloat16)
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I), dtype=torch.uint8, device="cuda")
+    h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    trace = torch.empty((L, m, H), dtype=torch.bfloat16, device="cuda")
+    ctx.verify_pass(arr, H, I, h0[:m], ws, h_out, trace=trace)
+    torch.cuda.synchronize()
+    t = trace.float()
+    assert torch.isfinite(t).all()
+    rms = t.pow(2).mean(dim=(1, 2)).sqrt().cpu().numpy()
+    log("rms by layer: first %.3f last %.3f max %.3f" % (rms[0], rms[-1], rms.max()))
+    assert rms.max() < 8.0 and rms.min() > 0.125

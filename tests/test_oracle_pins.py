@@ -337,5 +337,6 @@ def test_glue_against_library(oracle_mod):
     y = (g.standard_normal(50000) * 30).astype(np.float32)
     cst = np.float32(1.0 / math.sqrt(5120.0))
     assert np.array_equal(oracle_mod.glue_scale(x, cst), torch_bf16_bits(x * cst))
-    ref = torch_bf16_bits((x * cst) * (y * cst))
-    assert np.array_equal(oracle_mod.glue_mul(x, y, cst), ref)
+    c2 = np.float32(1.0 / math.sqrt(2 * 5120.0))
+    ref = torch_bf16_bits((x * c2) + (y * c2))
+    assert np.array_equal(oracle_mod.glue_sum(x, y, c2), ref)
