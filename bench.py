@@ -43,6 +43,14 @@ def layer_weight_bytes():
     return int((4 * H * H + 2 * I * H + H * I) * BYTES_PER_WEIGHT)
 
 
+def interleave_tiles(torch, w):
+    """[gate; up] (rows) -> 16-row tiles alternating gate, up."""
+    n, k = w.shape
+    half = n // 2
+    return torch.stack([w[:half].reshape(half // 16, 16, k), w[half:].reshape(half // 16, 16, k)],
+                       dim=1).reshape(n, k)
+
+
 def build_stack(torch, nv, synth, ctx, layers):
     """Quantise and pack `layers` layers of synthetic N(0,1) weights on the GPU."""
     scratch = torch.empty((2 * I, H), dtype=torch.float32, device="cuda")
@@ -57,6 +65,8 @@ def build_stack(torch, nv, synth, ctx, layers):
             for i, part in enumerate(parts):
                 synth.weights_f32_cuda(rows, k, seed=0, stream="L%d/%s" % (l, part),
                                        out=w[i * rows:(i + 1) * rows])
+            if name == "gate_up":  # the pass takes gate and up interleaved in 16-row tiles
+                w = interleave_tiles(torch, w)
             codes, scales = ctx.quantize(w)
             mats[name] = ctx.pack(codes, scales, n, k)
             del codes, scales
@@ -117,7 +127,8 @@ def gemm_event_timing(torch, ctx, packed, h0, m, passes=2):
                 elif name == "gate_up":
                     a_t = ctx.glue_scale(o, c_h)
                 elif name == "down":
-                    a_t = ctx.glue_sum(gu[:, :I], gu[:, I:], c_2)
+                    t = gu.view(m, I // 16, 2, 16)
+                    a_t = ctx.glue_sum(t[:, :, 0].reshape(m, I), t[:, :, 1].reshape(m, I), c_2)
                 else:
                     a_t = h
                 e0 = torch.cuda.Event(enable_timing=True)

@@ -164,7 +164,9 @@ int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64_t m, char 
  * codes and scales, cycled so timing does not hit a cache-resident copy; it
  * runs `warmup` untimed launches, then `reps` launches each between a pair of
  * HIP events on an internal stream, and writes the median duration in
- * microseconds to us_out[M - m_lo]. Synchronous. */
+ * microseconds to us_out[M - m_lo]. The activations are packed once per M
+ * (as the chained pass does), so each timed launch is the GEMM kernel alone.
+ * Synchronous. */
 int nvfp4v_staircase(nvfp4v_ctx *ctx, int64_t n, int64_t k, int m_lo, int m_hi, int warmup,
                      int reps, size_t rotate_bytes, double *us_out);
 
@@ -178,7 +180,9 @@ int nvfp4v_staircase(nvfp4v_ctx *ctx, int64_t n, int64_t k, int m_lo, int m_hi, 
  * nvfp4v_pack:
  *   qkv     [3H x H]  q, k and v stacked along N (rows 0..H-1 are q, ...)
  *   o       [H x H]
- *   gate_up [2I x H]  gate rows 0..I-1, then up rows
+ *   gate_up [2I x H]  gate and up interleaved in 16-row tiles: packed rows
+ *                     32t..32t+15 are gate rows 16t..16t+15 and rows
+ *                     32t+16..32t+31 are up rows 16t..16t+15
  *   down    [H x I]
  * with one fp32 tensor scale per packed matrix. */
 typedef struct nvfp4v_layer {
@@ -212,9 +216,12 @@ size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter);
  *   d   = GEMM(d_in, down);      h    = glue_scale(d, c_i)
  * h0 is bf16 [M][H]; the last layer's h goes to h_out (bf16 [M][H]). If trace
  * is not NULL, layer l's output h is also copied to trace[l][M][H]. Every
- * glue map is linear, so activations keep an O(1) RMS over the stack. After the
- * call returns, the workspace holds the last layer's fp32 GEMM outputs
- * (qkv [M][3H] at offset 0, then o, gu, d, each 256-byte aligned).
+ * glue map is linear, so activations keep an O(1) RMS over the stack. Each
+ * glue step runs in the epilogue of the GEMM that produces its input (4 kernel
+ * launches per layer, plus one that packs h0). After the call returns, the
+ * workspace holds the last layer's fp32 GEMM outputs (qkv [M][3H] at offset 0,
+ * then o [M][H], gu [M][2I] with gate columns 0..I-1 and up columns I..2I-1,
+ * d [M][H], each 256-byte aligned).
  * Does not allocate or synchronise; safe to capture in a HIP graph.
  * Errors: INVALID_ARG, SHAPE (H or I not a multiple of 16), M_RANGE, ALIGN,
  * WORKSPACE, HIP, FAULT. */

@@ -36,6 +36,9 @@
 //    paper": the 4-bit kernels keep a fixed reduction order). No float atomics.
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
+
+#include <hip/hip_bf16.h>
 
 #include "internal.h"
 
@@ -137,6 +140,89 @@ constexpr int waves_per_simd() {
   return MB == 1 ? 3 : 2;
 }
 
+__device__ inline uint16_t bf16_bits(float x) {
+  const __hip_bfloat16 b = __float2bfloat16(x);  // round to nearest even
+  uint16_t u;
+  __builtin_memcpy(&u, &b, 2);
+  return u;
+}
+
+__device__ inline float glue_pair(float g, float u, float c) {
+#pragma clang fp contract(off)
+  const float pg = g * c;
+  const float pu = u * c;
+  return pg + pu;
+}
+
+// Four consecutive bf16 outputs (column j, j % 4 == 0) of row m: into the next
+// GEMM's packed activations and the optional row-major copies.
+__device__ inline void store_next(const Epilogue &epi, int mblocks, int m, int j, int cols,
+                                  const float (&o)[4]) {
+  const uint32_t lo = (uint32_t)bf16_bits(o[0]) | ((uint32_t)bf16_bits(o[1]) << 16);
+  const uint32_t hi = (uint32_t)bf16_bits(o[2]) | ((uint32_t)bf16_bits(o[3]) << 16);
+  const uint2 v = make_uint2(lo, hi);
+  *reinterpret_cast<uint2 *>(epi.act + act_offset(m, j, mblocks)) = v;
+  if (epi.rm0) *reinterpret_cast<uint2 *>(epi.rm0 + (size_t)m * cols + j) = v;
+  if (epi.rm1) *reinterpret_cast<uint2 *>(epi.rm1 + (size_t)m * cols + j) = v;
+}
+
+// Final values of the work-group's tiles are red[w][r][mb][l] summed over the
+// first nw slots (wave order). Writes C (times ts) and the fused glue.
+template <int MB, int R>
+__device__ inline void epilogue(const f32x4 *red, int nw, int tid, int M, int N, int nrt, int rt0,
+                                float ts, float *C, const Epilogue &epi) {
+  if (epi.mode == EPI_PAIR) {
+    const int half = N / 2;
+    for (int it = tid; it < (R / 2) * MB * 64; it += WG_THREADS) {
+      const int p = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+      f32x4 vg = red[((0 * R + 2 * p) * MB + mb) * 64 + l];
+      f32x4 vu = red[((0 * R + 2 * p + 1) * MB + mb) * 64 + l];
+      for (int wv = 1; wv < nw; ++wv) {
+        vg += red[((wv * R + 2 * p) * MB + mb) * 64 + l];
+        vu += red[((wv * R + 2 * p + 1) * MB + mb) * 64 + l];
+      }
+      const int m = mb * 16 + (l & 15), rtg = rt0 + 2 * p;
+      if (m >= M || rtg + 1 >= nrt) continue;
+      const int j0 = (rtg / 2) * ROWS_PER_TILE + 4 * (l >> 4);
+      if (j0 >= half) continue;
+      vg *= ts;
+      vu *= ts;
+      if (epi.write_c) {
+        *reinterpret_cast<f32x4 *>(C + (size_t)m * N + j0) = vg;
+        *reinterpret_cast<f32x4 *>(C + (size_t)m * N + half + j0) = vu;
+      }
+      const float o[4] = {glue_pair(vg[0], vu[0], epi.c), glue_pair(vg[1], vu[1], epi.c),
+                          glue_pair(vg[2], vu[2], epi.c), glue_pair(vg[3], vu[3], epi.c)};
+      store_next(epi, MB, m, j0, half, o);
+    }
+    return;
+  }
+  for (int it = tid; it < R * MB * 64; it += WG_THREADS) {
+    const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+    f32x4 v = red[((0 * R + r) * MB + mb) * 64 + l];
+    for (int wv = 1; wv < nw; ++wv) v += red[((wv * R + r) * MB + mb) * 64 + l];
+    // lane l of a tile holds D[n = 16 rt + 4 (l / 16) + i][m = 16 mb + l % 16]
+    const int m = mb * 16 + (l & 15);
+    const int rt = rt0 + r;
+    const int n0 = rt * ROWS_PER_TILE + 4 * (l >> 4);
+    if (m >= M || rt >= nrt || n0 >= N) continue;
+    v *= ts;
+    if (epi.write_c) {
+      float *dst = C + (size_t)m * N + n0;
+      if ((N & 3) == 0) {
+        *reinterpret_cast<f32x4 *>(dst) = v;
+      } else {
+        for (int i = 0; i < 4; ++i)
+          if (n0 + i < N) dst[i] = v[i];
+      }
+    }
+    if (epi.mode == EPI_SCALE && n0 >= epi.col0 && n0 < epi.col1) {
+      const float o[4] = {v[0] * epi.c, v[1] * epi.c, v[2] * epi.c, v[3] * epi.c};
+      store_next(epi, MB, m, n0 - epi.col0, epi.col1 - epi.col0, o);
+    }
+  }
+}
+
 // ABUF = 2 double-buffers the activation fragments; with ABUF = 1 the next
 // k-tile's fragments are loaded after the last use of the current ones (large
 // M, where two copies do not fit in registers).
@@ -144,7 +230,8 @@ template <int MB, int R, int ABUF>
 __global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MB, R>())))
 void k_gemm(const uint8_t *__restrict__ act, int M, int act_bytes, const uint8_t *__restrict__ W,
             int N, int nrt, int nkt, int kts_per_split, int ksplit, float ts,
-            float *__restrict__ C, float *__restrict__ part, unsigned *__restrict__ counters) {
+            float *__restrict__ C, float *__restrict__ part, unsigned *__restrict__ counters,
+            Epilogue epi) {
   extern __shared__ __align__(16) f32x4 red[];  // [WG_WAVES][R][MB][64]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
@@ -210,7 +297,8 @@ void k_gemm(const uint8_t *__restrict__ act, int M, int act_bytes, const uint8_t
     }
   }
 
-  // Sum the 4 waves' tiles in wave order.
+  // Sum the 4 waves' tiles in wave order (LDS), then either finish here
+  // (ksplit == 1) or exchange partial tiles with the other splits.
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -219,68 +307,72 @@ void k_gemm(const uint8_t *__restrict__ act, int M, int act_bytes, const uint8_t
 
   const int npad = nrt * ROWS_PER_TILE;
   constexpr int ITEMS = R * MB * 64;
-  for (int it = tid; it < ITEMS; it += WG_THREADS) {
-    const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
-    f32x4 v = red[((0 * R + r) * MB + mb) * 64 + l];
+  int nw = WG_WAVES;
+  if (ksplit > 1) {
+    for (int it = tid; it < ITEMS; it += WG_THREADS) {
+      const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+      f32x4 v = red[((0 * R + r) * MB + mb) * 64 + l];
 #pragma unroll
-    for (int wv = 1; wv < WG_WAVES; ++wv) v += red[((wv * R + r) * MB + mb) * 64 + l];
-    // lane l of a tile holds D[n = 16 rt + 4 (l / 16) + i][m = 16 mb + l % 16]
-    const int m = mb * 16 + (l & 15);
-    const int rt = rt0 + r;
-    const int n0 = rt * ROWS_PER_TILE + 4 * (l >> 4);
-    if (m >= M || rt >= nrt) continue;
-    if (ksplit == 1) {
-      float *dst = C + (size_t)m * N + n0;
-      if ((N & 3) == 0) {
-        if (n0 < N) *reinterpret_cast<f32x4 *>(dst) = v * ts;
-      } else {
-        for (int i = 0; i < 4; ++i)
-          if (n0 + i < N) dst[i] = v[i] * ts;
-      }
-    } else {
-      float *dst = part + ((size_t)ks * M + m) * npad + n0;
+      for (int wv = 1; wv < WG_WAVES; ++wv) v += red[((wv * R + r) * MB + mb) * 64 + l];
+      const int m = mb * 16 + (l & 15), rt = rt0 + r;
+      if (m >= M || rt >= nrt) continue;
+      float *dst = part + ((size_t)ks * M + m) * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __hip_atomic_store(dst + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
+    // The partial stores have reached memory once this wave's counters drain.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __shared__ unsigned s_ticket;
+    if (tid == 0)
+      s_ticket = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __syncthreads();
+    if (s_ticket != (unsigned)(ksplit - 1)) return;
+    // Last to arrive: sum the splits in order 0..ksplit-1 into slot 0.
+    for (int it = tid; it < ITEMS; it += WG_THREADS) {
+      const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+      const int m = mb * 16 + (l & 15), rt = rt0 + r;
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (m < M && rt < nrt) {
+        const float *src = part + (size_t)m * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int s2 = 1; s2 < ksplit; ++s2) {
+          const float *s2p = src + (size_t)s2 * M * npad;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] += __hip_atomic_load(s2p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+      }
+      red[((0 * R + r) * MB + mb) * 64 + l] = v;
+    }
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    nw = 1;
   }
-  if (ksplit == 1) return;
-
-  // The partial stores have reached memory once this wave's counters drain.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  __shared__ unsigned s_ticket;
-  if (tid == 0)
-    s_ticket = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  __syncthreads();
-  if (s_ticket != (unsigned)(ksplit - 1)) return;
-  const int rows = R * ROWS_PER_TILE;
-  for (int e = tid; e < M * rows; e += WG_THREADS) {
-    const int m = e / rows, nn = rt0 * ROWS_PER_TILE + (e - m * rows);
-    if (nn >= N) continue;
-    float sum = __hip_atomic_load(part + (size_t)m * npad + nn, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_SYSTEM);
-    for (int s2 = 1; s2 < ksplit; ++s2)
-      sum += __hip_atomic_load(part + ((size_t)s2 * M + m) * npad + nn, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_SYSTEM);
-    C[(size_t)m * N + nn] = sum * ts;
-  }
-  if (tid == 0) __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  epilogue<MB, R>(red, nw, tid, M, N, nrt, rt0, ts, C, epi);
 }
 
 typedef void (*GemmKernel)(const uint8_t *, int, int, const uint8_t *, int, int, int, int, int,
-                           float, float *, float *, unsigned *);
+                           float, float *, float *, unsigned *, Epilogue);
 
 GemmKernel pick_kernel(int mb, int r) {
-  switch (mb * 8 + r) {
-    case 1 * 8 + 2: return k_gemm<1, 2, 2>;
-    case 1 * 8 + 4: return k_gemm<1, 4, 2>;
-    case 2 * 8 + 2: return k_gemm<2, 2, 2>;
-    case 2 * 8 + 4: return k_gemm<2, 4, 2>;
-    case 3 * 8 + 2: return k_gemm<3, 2, 1>;
-    case 3 * 8 + 4: return k_gemm<3, 4, 1>;
-    case 4 * 8 + 2: return k_gemm<4, 2, 1>;
-    case 4 * 8 + 4: return k_gemm<4, 4, 1>;
+  switch (mb * 16 + r) {
+    case 1 * 16 + 1: return k_gemm<1, 1, 2>;
+    case 1 * 16 + 2: return k_gemm<1, 2, 2>;
+    case 1 * 16 + 4: return k_gemm<1, 4, 2>;
+    case 1 * 16 + 8: return k_gemm<1, 8, 2>;
+    case 2 * 16 + 1: return k_gemm<2, 1, 2>;
+    case 2 * 16 + 2: return k_gemm<2, 2, 2>;
+    case 2 * 16 + 4: return k_gemm<2, 4, 2>;
+    case 2 * 16 + 8: return k_gemm<2, 8, 1>;
+    case 3 * 16 + 1: return k_gemm<3, 1, 1>;
+    case 3 * 16 + 2: return k_gemm<3, 2, 1>;
+    case 3 * 16 + 4: return k_gemm<3, 4, 1>;
+    case 4 * 16 + 1: return k_gemm<4, 1, 1>;
+    case 4 * 16 + 2: return k_gemm<4, 2, 1>;
+    case 4 * 16 + 4: return k_gemm<4, 4, 1>;
     default: return nullptr;
   }
 }
@@ -308,23 +400,46 @@ __global__ void k_pack_act(const uint16_t *__restrict__ A, int M, int K, int mbl
 
 namespace nvfp4v {
 
-// Tile table: R (row tiles per work-group, sharing one activation fragment),
-// then enough work-groups along K that about 1.5 work-groups per CU exist,
-// keeping at least 2 k-tiles per wave.
+// Tile table for gfx950, from a sweep of R (row tiles per work-group, sharing
+// one activation fragment) and ksplit (work-groups along K) over the layer
+// shapes [15360|5120|34816 x 5120], [5120 x 17408] and [151936 x 5120] at
+// M = 1, 16, 32, 64 (median of 9 timed launches over 1 GiB of rotated weight
+// copies each):
+//  * splitting K across work-groups only pays for K-heavy, narrow matrices
+//    (down: 3 splits); everywhere else one work-group covers all of K;
+//  * R = 2 is best up to about 4096 row tiles at M <= 32; very wide matrices
+//    (the 151936-row head) want R = 4 at M <= 16 and R = 8 at M <= 32;
+//  * at M > 32, R = 4 except for the narrowest matrices (R = 2).
+// NVFP4V_PLAN="r=<R>,ks=<ksplit>" overrides both (used by tuning sweeps).
 int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
   p->mblocks = (int)((m + 15) / 16);
-  p->rb = 4;
   p->waves = WG_WAVES;
-  p->grid_x = (int)((L.nrt + p->rb - 1) / p->rb);
+  const int64_t nrt = L.nrt;
   const int nkt = (int)L.nkt;
-  const int target = std::max(1, (3 * std::max(1, ctx->num_cus)) / 2);
-  int ks = std::max(1, (target + p->grid_x - 1) / p->grid_x);
-  ks = std::min(ks, std::max(1, nkt / (2 * WG_WAVES)));
-  int per = (nkt + ks - 1) / ks;
-  ks = (nkt + per - 1) / per;
-  p->ksplit = ks;
-  p->ktiles_per_split = per;
-  p->grid_y = ks;
+  if (p->mblocks == 1)
+    p->rb = nrt >= 4096 && m > 1 ? 4 : 2;
+  else if (p->mblocks == 2)
+    p->rb = nrt >= 4096 ? 8 : 2;
+  else
+    p->rb = nrt >= 640 ? 4 : 2;
+  int want_ks = (nkt >= 48 && nrt <= 640) ? 3 : 1;
+  if (const char *ov = std::getenv("NVFP4V_PLAN")) {
+    int r = 0, k2 = 0;
+    if (std::sscanf(ov, "r=%d,ks=%d", &r, &k2) == 2 && (r == 1 || r == 2 || r == 4 || r == 8)) {
+      p->rb = r;
+      want_ks = k2 > 0 ? k2 : 1;
+    }
+  }
+  (void)ctx;
+  int force_ks = want_ks;
+  if (!pick_kernel(p->mblocks, p->rb)) p->rb = 4;
+  p->grid_x = (int)((L.nrt + p->rb - 1) / p->rb);
+  {
+    const int ks = std::min(force_ks, nkt);
+    const int per = (nkt + ks - 1) / ks;
+    p->ktiles_per_split = per;
+    p->ksplit = p->grid_y = (nkt + per - 1) / per;
+  }
   p->lds_bytes = (size_t)WG_WAVES * p->rb * p->mblocks * 64 * sizeof(f32x4);
   return NVFP4V_OK;
 }
@@ -339,12 +454,17 @@ int launch_pack_act(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, ui
 }
 
 int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
-                int64_t n, float ts, float *c, hipStream_t stream) {
+                int64_t n, float ts, float *c, hipStream_t stream, const Epilogue &epi) {
   Layout L;
   if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
   Plan p;
   int rc = make_plan(ctx, L, m, &p);
   if (rc) return rc;
+  if (epi.mode == EPI_PAIR && (p.rb & 1)) {  // (gate, up) row-tile pairs need an even R
+    p.rb = 2;
+    p.grid_x = (int)((L.nrt + p.rb - 1) / p.rb);
+    p.lds_bytes = (size_t)WG_WAVES * p.rb * p.mblocks * 64 * sizeof(f32x4);
+  }
   if (p.ksplit > 1) {
     const size_t need = (size_t)p.ksplit * (size_t)m * (size_t)(L.nrt * ROWS_PER_TILE);
     if (need > ctx->partial_floats || (size_t)p.grid_x > ctx->n_counters) return NVFP4V_E_WORKSPACE;
@@ -355,7 +475,7 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
   hipLaunchKernelGGL(kern, dim3((unsigned)p.grid_x, (unsigned)p.grid_y), dim3(WG_THREADS),
                      p.lds_bytes, stream, act, (int)m, (int)act_packed_bytes(m, k),
                      (const uint8_t *)packed, (int)n, (int)L.nrt, (int)L.nkt, p.ktiles_per_split,
-                     p.ksplit, ts, c, ctx->partials, ctx->counters);
+                     p.ksplit, ts, c, ctx->partials, ctx->counters, epi);
   return hip_status(ctx, hipGetLastError());
 }
 

@@ -193,7 +193,25 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p);
 // Enqueue A (row-major bf16) -> packed activations (no argument checks).
 int launch_pack_act(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
                     hipStream_t stream);
+// Fused epilogue of a GEMM in the chained pass: besides (optionally) writing
+// the fp32 C, turn C into the next GEMM's bf16 input, in packed-activation
+// order, and optionally into up to two row-major bf16 copies.
+//   EPI_NONE:  C only.
+//   EPI_SCALE: for columns [col0, col1): out[m][j - col0] = bf16(C[m][j] * c).
+//   EPI_PAIR:  row tiles come in (gate, up) pairs (tile 2t = gate rows
+//              16t..16t+15, tile 2t+1 = the matching up rows);
+//              out[m][j] = bf16(gate * c + up * c) (no fused multiply-add), and
+//              C is written in natural order [gate | up].
+enum EpiMode { EPI_NONE = 0, EPI_SCALE = 1, EPI_PAIR = 2 };
+struct Epilogue {
+  int mode = EPI_NONE;
+  int col0 = 0, col1 = 0;
+  float c = 1.f;
+  uint8_t *act = nullptr;  // packed activations of the next GEMM (its K = out columns)
+  uint16_t *rm0 = nullptr, *rm1 = nullptr;  // optional row-major bf16 copies [M][out cols]
+  int write_c = 1;
+};
 // Enqueue the GEMM on packed activations (no argument checks).
 int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
-                int64_t n, float ts, float *c, hipStream_t stream);
+                int64_t n, float ts, float *c, hipStream_t stream, const Epilogue &epi = Epilogue());
 }  // namespace nvfp4v

@@ -5,9 +5,11 @@
 //
 // The pages give neither the layer shapes nor the non-GEMM operations, so the
 // stack is a uniform stand-in: per layer, a fused q|k|v projection
-// [3H x H], o [H x H], a fused gate|up projection [2I x H] and down [H x I],
-// joined by elementwise glue that keeps activations O(1) (no reductions, no
-// activation function, since the pages name none):
+// [3H x H], o [H x H], a fused gate|up projection [2I x H] (gate and up rows
+// interleaved in 16-row tiles) and down [H x I], joined by elementwise glue
+// that keeps activations O(1) (no reductions, no activation function, since the
+// pages name none). The glue runs in the epilogue of the GEMM that produces
+// its input:
 //   qkv = h Wqkv^T;               o_in = bf16(v * H^-1/2)   (one-key attention)
 //   o   = o_in Wo^T;              g_in = bf16(o * H^-1/2)
 //   gu  = g_in Wgu^T;             d_in = bf16(gate * (2H)^-1/2 + up * (2H)^-1/2)
@@ -182,20 +184,21 @@ extern "C" int nvfp4v_verify_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, i
   const float c2h = (float)(1.0 / std::sqrt(2.0 * (double)hidden));
   const int64_t H = hidden, I = inter;
   int rc = launch_pack_act(ctx, h0, m, H, w.act_h, stream);
+  // Each GEMM's epilogue writes the next GEMM's packed activations (the glue
+  // above), so a layer is four launches.
+  Epilogue e_o, e_g, e_d, e_h;
+  e_o.mode = EPI_SCALE, e_o.col0 = (int)(2 * H), e_o.col1 = (int)(3 * H), e_o.c = ch, e_o.act = w.act_o;
+  e_g.mode = EPI_SCALE, e_g.col0 = 0, e_g.col1 = (int)H, e_g.c = ch, e_g.act = w.act_g;
+  e_d.mode = EPI_PAIR, e_d.c = c2h, e_d.act = w.act_d;
+  e_h.mode = EPI_SCALE, e_h.col0 = 0, e_h.col1 = (int)H, e_h.c = ci, e_h.act = w.act_h;
   for (int l = 0; l < n_layers && rc == NVFP4V_OK; ++l) {
     const nvfp4v_layer &L = layers[l];
-    uint16_t *rm0 = (l == n_layers - 1) ? h_out : nullptr;
-    uint16_t *rm1 = trace ? trace + (size_t)l * m * H : nullptr;
-    rc = launch_gemm(ctx, w.act_h, m, H, L.qkv, 3 * H, L.ts_qkv, w.qkv, stream);
-    if (!rc) rc = launch_glue_pa(ctx, w.qkv + 2 * H, 3 * H, nullptr, 0, m, H, ch, w.act_o, nullptr,
-                                 nullptr, stream);
-    if (!rc) rc = launch_gemm(ctx, w.act_o, m, H, L.o, H, L.ts_o, w.o, stream);
-    if (!rc) rc = launch_glue_pa(ctx, w.o, H, nullptr, 0, m, H, ch, w.act_g, nullptr, nullptr, stream);
-    if (!rc) rc = launch_gemm(ctx, w.act_g, m, H, L.gate_up, 2 * I, L.ts_gate_up, w.gu, stream);
-    if (!rc) rc = launch_glue_pa(ctx, w.gu, 2 * I, w.gu + I, 2 * I, m, I, c2h, w.act_d, nullptr,
-                                 nullptr, stream);
-    if (!rc) rc = launch_gemm(ctx, w.act_d, m, I, L.down, H, L.ts_down, w.d, stream);
-    if (!rc) rc = launch_glue_pa(ctx, w.d, H, nullptr, 0, m, H, ci, w.act_h, rm0, rm1, stream);
+    e_h.rm0 = (l == n_layers - 1) ? h_out : nullptr;
+    e_h.rm1 = trace ? trace + (size_t)l * m * H : nullptr;
+    rc = launch_gemm(ctx, w.act_h, m, H, L.qkv, 3 * H, L.ts_qkv, w.qkv, stream, e_o);
+    if (!rc) rc = launch_gemm(ctx, w.act_o, m, H, L.o, H, L.ts_o, w.o, stream, e_g);
+    if (!rc) rc = launch_gemm(ctx, w.act_g, m, H, L.gate_up, 2 * I, L.ts_gate_up, w.gu, stream, e_d);
+    if (!rc) rc = launch_gemm(ctx, w.act_d, m, I, L.down, H, L.ts_down, w.d, stream, e_h);
   }
   return rc;
 }

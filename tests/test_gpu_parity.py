@@ -252,3 +252,21 @@ def test_prepacked_activations_match(torch_cuda, ctx):
             assert act.numel() == nv.act_packed_bytes(m, k)
             got = ctx.verify_gemm_pa(act, m, k, packed, n)
             assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), (n, k, m)
+
+
+@pytest.mark.parametrize("plan", ["r=1,ks=1", "r=2,ks=3", "r=4,ks=2", "r=8,ks=1", "r=8,ks=4", "r=1,ks=9"])
+def test_plan_variants(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
+    """Every tile-table variant the dispatcher can pick agrees with the oracle."""
+    torch = torch_cuda
+    n, k = 272, 4608   # 17 row tiles (ragged for R = 2, 4, 8), 18 k-tiles
+    g = np.random.default_rng(31)
+    codes, scales = random_codes_scales(g, n, k)
+    a = synth.activations_bf16(64, k, seed=6, outliers=True)
+    c_ref, s_ref = oracle_mod.gemm(a, codes, scales, ts=1.25)
+    packed = pack_dev(torch, ctx, codes, scales, n, k)
+    a_dev = bf16_dev(torch, a)
+    monkeypatch.setenv("NVFP4V_PLAN", plan)
+    for m in (1, 16, 33, 64):
+        log("plan %s M=%d: %s" % (plan, m, ctx.describe_plan(n, k, m)))
+        c = ctx.verify_gemm(a_dev[:m], packed, n, k, ts=1.25).cpu().numpy()
+        assert_parity(oracle_mod, c, c_ref[:m], s_ref[:m], "plan %s M=%d" % (plan, m))

@@ -66,6 +66,9 @@ def small_stack(torch, ctx, layers, H, I, seed=0):
                                   ("gate_up", ("gate", "up"), 2 * I, H), ("down", ("down",), H, I)):
             w = torch.cat([synth.weights_f32_cuda(n // len(parts), k, seed=seed,
                                                   stream="t%d/%s" % (l, p)) for p in parts])
+            if name == "gate_up":  # gate and up interleaved in 16-row tiles
+                w = torch.stack([w[: n // 2].reshape(n // 32, 16, k), w[n // 2:].reshape(n // 32, 16, k)],
+                                dim=1).reshape(n, k)
             codes, scales = ctx.quantize(w)
             mats[name] = ctx.pack(codes, scales, n, k)
         packed.append(mats)
@@ -84,7 +87,9 @@ def manual_chain(torch, ctx, packed, h0, H, I):
         qkv = ctx.verify_gemm(h, mats["qkv"], 3 * H, H)
         o = ctx.verify_gemm(ctx.glue_scale(qkv[:, 2 * H:], c_h), mats["o"], H, H)
         gu = ctx.verify_gemm(ctx.glue_scale(o, c_h), mats["gate_up"], 2 * I, H)
-        d = ctx.verify_gemm(ctx.glue_sum(gu[:, :I], gu[:, I:], c_2), mats["down"], H, I)
+        t = gu.view(gu.shape[0], I // 16, 2, 16)  # plain GEMM output follows the interleaved rows
+        gate, up = t[:, :, 0].reshape(-1, I).contiguous(), t[:, :, 1].reshape(-1, I).contiguous()
+        d = ctx.verify_gemm(ctx.glue_sum(gate, up, c_2), mats["down"], H, I)
         h = ctx.glue_scale(d, c_i)
         outs.append(h)
     return outs
@@ -104,6 +109,17 @@ def test_pass_equals_composition(torch_cuda, ctx, m):
     for l in range(L):
         assert torch.equal(trace[l].view(torch.int16), ref[l].view(torch.int16)), "layer %d" % l
     assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16))
+    # the workspace holds the last layer's fp32 outputs; gu in natural [gate | up] order
+    off = 0
+    sizes = [m * 3 * H * 4, m * H * 4, m * 2 * I * 4, m * H * 4]
+    outs = []
+    for sz in sizes:
+        outs.append(ws[off:off + sz].view(torch.float32))
+        off += (sz + 255) // 256 * 256
+    last = packed[-1]
+    h_prev = ref[-2] if L > 1 else h0[:m]
+    qkv = ctx.verify_gemm(h_prev, last["qkv"], 3 * H, H)
+    assert torch.equal(outs[0].view(m, 3 * H), qkv)
 
 
 def test_graph_replays_equal_eager(torch_cuda, ctx):
