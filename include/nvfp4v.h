@@ -64,6 +64,7 @@ extern "C" {
 #define NVFP4V_E_FAULT (-6)       /* injected by NVFP4V_FAULT=launch (testing) */
 #define NVFP4V_E_NONFINITE (-7)   /* quantiser input holds NaN or Inf          */
 #define NVFP4V_E_WORKSPACE (-8)   /* the request exceeds the context workspace */
+#define NVFP4V_E_TIMEOUT (-9)     /* a persistent pass gave up at a grid barrier */
 
 #define NVFP4V_MAX_M 64
 
@@ -203,12 +204,26 @@ int nvfp4v_glue_sum(nvfp4v_ctx *ctx, const float *x_dev, int64_t ldx, const floa
                     int64_t ldy, int64_t rows, int64_t cols, float c, uint16_t *out_dev,
                     hipStream_t stream);
 
-/* Bytes of caller-owned device workspace nvfp4v_verify_pass needs (0 for bad
- * arguments): the fp32 outputs and bf16 inputs of one layer, plus two bf16
- * hidden-state buffers. */
-size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter);
+/* Bytes of caller-owned device workspace nvfp4v_verify_pass needs for
+ * n_layers layers (0 for bad arguments): the fp32 outputs of one layer plus
+ * one block of packed bf16 activations per layer and GEMM (about 1 MiB per
+ * layer at M = 16, H = 5120, I = 17408). */
+size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter, int n_layers);
 
-/* Enqueue the whole pass on `stream`: for each layer, with c_h = H^-1/2,
+/* How nvfp4v_verify_pass schedules its GEMMs (per context; default CHAIN):
+ *   NVFP4V_PASS_CHAIN       one GEMM launch per projection, four per layer,
+ *                           stream-ordered;
+ *   NVFP4V_PASS_PERSISTENT  one cooperatively launched persistent kernel per
+ *                           32 layers whose work-groups meet at a grid barrier
+ *                           between dependent GEMMs.
+ * Both compute the same values bit for bit. Errors: INVALID_ARG. */
+#define NVFP4V_PASS_CHAIN 0
+#define NVFP4V_PASS_PERSISTENT 1
+int nvfp4v_set_pass_mode(nvfp4v_ctx *ctx, int mode);
+int nvfp4v_get_pass_mode(const nvfp4v_ctx *ctx);
+
+/* Enqueue the whole pass on `stream`: one packing kernel, then the layers'
+ * GEMMs as the context's pass mode schedules them. For each layer, with c_h = H^-1/2,
  * c_2 = (2H)^-1/2 and c_i = I^-1/2 (fp32, rounded from fp64):
  *   qkv = GEMM(h, qkv);          o_in = glue_scale(v part of qkv, c_h)
  *   o   = GEMM(o_in, o);         g_in = glue_scale(o, c_h)
@@ -217,18 +232,34 @@ size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter);
  * h0 is bf16 [M][H]; the last layer's h goes to h_out (bf16 [M][H]). If trace
  * is not NULL, layer l's output h is also copied to trace[l][M][H]. Every
  * glue map is linear, so activations keep an O(1) RMS over the stack. Each
- * glue step runs in the epilogue of the GEMM that produces its input (4 kernel
- * launches per layer, plus one that packs h0). After the call returns, the
+ * glue step runs in the epilogue of the GEMM that produces its input. In
+ * persistent mode a barrier wait that exceeds 2 s (it cannot while the launch
+ * is co-resident) ends the kernel early and sets an error flag that
+ * nvfp4v_pass_status reports; the outputs are then undefined. After the call returns, the
  * workspace holds the last layer's fp32 GEMM outputs (qkv [M][3H] at offset 0,
  * then o [M][H], gu [M][2I] with gate columns 0..I-1 and up columns I..2I-1,
  * d [M][H], each 256-byte aligned).
- * Does not allocate or synchronise; safe to capture in a HIP graph.
+ * Does not allocate or synchronise. Calls on one context must not overlap.
  * Errors: INVALID_ARG, SHAPE (H or I not a multiple of 16), M_RANGE, ALIGN,
  * WORKSPACE, HIP, FAULT. */
 int nvfp4v_verify_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_t hidden,
                        int64_t inter, const uint16_t *h0_dev, int64_t m, void *ws_dev,
                        size_t ws_bytes, uint16_t *h_out_dev, uint16_t *trace_dev,
                        hipStream_t stream);
+
+/* Synchronise the device and report whether the last persistent pass on this
+ * context finished (NVFP4V_OK) or gave up at a barrier (NVFP4V_E_TIMEOUT). */
+int nvfp4v_pass_status(nvfp4v_ctx *ctx);
+/* Work-groups of the last persistent pass launch (0 before the first). */
+int nvfp4v_last_pass_grid(const nvfp4v_ctx *ctx);
+/* Phase timeline of the last pass, for profiling (only when the context was
+ * created with NVFP4V_PASS_TRACE=1 in the environment, else INVALID_ARG):
+ * synchronously copies up to max_words words into out_host, laid out as
+ * [phase][1024 work-group slots][2]: the 100 MHz real-time clock when the
+ * work-group started the phase and when it finished its work in it (before
+ * the barrier). *phases and *groups receive the phase and work-group counts. */
+int nvfp4v_pass_timeline(nvfp4v_ctx *ctx, uint64_t *out_host, size_t max_words, int *phases,
+                         int *groups);
 
 /* ---- Measurement helpers ------------------------------------------------- */
 

@@ -25,6 +25,9 @@ E_HIP = -5
 E_FAULT = -6
 E_NONFINITE = -7
 E_WORKSPACE = -8
+E_TIMEOUT = -9
+PASS_CHAIN = 0
+PASS_PERSISTENT = 1
 MAX_M = 64
 
 _lib = None
@@ -71,7 +74,12 @@ def load():
                                      c.c_size_t, p]
     lib.nvfp4v_glue_scale.argtypes = [p, p, i64, i64, i64, c.c_float, p, p]
     lib.nvfp4v_glue_sum.argtypes = [p, p, i64, p, i64, i64, i64, c.c_float, p, p]
-    lib.nvfp4v_pass_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.nvfp4v_pass_workspace_bytes.argtypes = [i64, i64, i64, c.c_int]
+    lib.nvfp4v_pass_status.argtypes = [p]
+    lib.nvfp4v_last_pass_grid.argtypes = [p]
+    lib.nvfp4v_set_pass_mode.argtypes = [p, c.c_int]
+    lib.nvfp4v_get_pass_mode.argtypes = [p]
+    lib.nvfp4v_pass_timeline.argtypes = [p, p, c.c_size_t, p, p]
     lib.nvfp4v_pass_workspace_bytes.restype = c.c_size_t
     lib.nvfp4v_verify_pass.argtypes = [p, p, c.c_int, i64, i64, p, i64, p, c.c_size_t, p, p, p]
     lib.nvfp4v_read_probe_sink_words.argtypes = [p]
@@ -268,6 +276,32 @@ class Context:
             "nvfp4v_verify_pass")
         return h_out
 
+    def pass_status(self) -> int:
+        """Synchronise; NVFP4V_OK, or E_TIMEOUT if the last pass gave up at a barrier."""
+        return int(load().nvfp4v_pass_status(self._h))
+
+    def set_pass_mode(self, mode: int) -> None:
+        """PASS_CHAIN (four GEMM launches per layer) or PASS_PERSISTENT."""
+        _check(load().nvfp4v_set_pass_mode(self._h, int(mode)), "set_pass_mode")
+
+    def get_pass_mode(self) -> int:
+        return int(load().nvfp4v_get_pass_mode(self._h))
+
+    def last_pass_grid(self) -> int:
+        return int(load().nvfp4v_last_pass_grid(self._h))
+
+    def pass_timeline(self):
+        """(start, done) real-time-clock stamps [phases, groups] of the last pass
+        (context created with NVFP4V_PASS_TRACE=1)."""
+        import numpy as np
+
+        buf = np.zeros(2 * 1024 * 512, np.uint64)
+        ph, gr = ctypes.c_int(), ctypes.c_int()
+        _check(load().nvfp4v_pass_timeline(self._h, _np_ptr(buf), buf.size, ctypes.byref(ph),
+                                           ctypes.byref(gr)), "nvfp4v_pass_timeline")
+        t = buf.reshape(512, 1024, 2)[: ph.value, : gr.value]
+        return t[:, :, 0], t[:, :, 1]
+
     # -- measurement helpers ------------------------------------------------
     def read_probe(self, buf, sink, stream=None):
         _check(load().nvfp4v_read_probe(self._h, _t_ptr(buf), buf.numel() * buf.element_size(),
@@ -304,8 +338,8 @@ class Layer(ctypes.Structure):
                 ("ts_gate_up", ctypes.c_float), ("ts_down", ctypes.c_float)]
 
 
-def pass_workspace_bytes(m: int, hidden: int, inter: int) -> int:
-    return int(load().nvfp4v_pass_workspace_bytes(m, hidden, inter))
+def pass_workspace_bytes(m: int, hidden: int, inter: int, n_layers: int) -> int:
+    return int(load().nvfp4v_pass_workspace_bytes(m, hidden, inter, n_layers))
 
 
 def exported_names():

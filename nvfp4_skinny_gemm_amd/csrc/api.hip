@@ -1,4 +1,5 @@
 // Context lifetime, status codes and shared host helpers of the C ABI.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -45,6 +46,14 @@ extern "C" int nvfp4v_create(nvfp4v_ctx **out, int device) {
   if (e == hipSuccess) e = hipMalloc((void **)&ctx->counters, kCounters * sizeof(unsigned));
   if (e == hipSuccess) e = hipMemset(ctx->counters, 0, kCounters * sizeof(unsigned));
   if (e == hipSuccess) e = hipMalloc((void **)&ctx->act, kActBytes);
+  if (e == hipSuccess) e = hipMalloc((void **)&ctx->pass_sync, PASS_SYNC_WORDS * sizeof(unsigned));
+  if (e == hipSuccess) e = hipMemset(ctx->pass_sync, 0, PASS_SYNC_WORDS * sizeof(unsigned));
+  const char *tl = std::getenv("NVFP4V_PASS_TRACE");
+  if (e == hipSuccess && tl && std::strcmp(tl, "1") == 0) {
+    ctx->pass_timeline_words = 2 * PASS_TIMELINE_WGS * PASS_TIMELINE_PHASES;
+    e = hipMalloc((void **)&ctx->pass_timeline, ctx->pass_timeline_words * sizeof(uint64_t));
+    if (e == hipSuccess) e = hipMemset(ctx->pass_timeline, 0, ctx->pass_timeline_words * sizeof(uint64_t));
+  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     int code = (int)e;
@@ -64,10 +73,34 @@ extern "C" void nvfp4v_destroy(nvfp4v_ctx *ctx) {
   if (ctx->partials) (void)hipFree(ctx->partials);
   if (ctx->counters) (void)hipFree(ctx->counters);
   if (ctx->act) (void)hipFree(ctx->act);
+  if (ctx->pass_sync) (void)hipFree(ctx->pass_sync);
+  if (ctx->pass_timeline) (void)hipFree(ctx->pass_timeline);
   delete ctx;
 }
 
 extern "C" int nvfp4v_last_hip_error(const nvfp4v_ctx *ctx) { return ctx ? ctx->last_hip : 0; }
+
+extern "C" int nvfp4v_set_pass_mode(nvfp4v_ctx *ctx, int mode) {
+  if (!ctx || (mode != NVFP4V_PASS_CHAIN && mode != NVFP4V_PASS_PERSISTENT)) return NVFP4V_E_INVALID_ARG;
+  ctx->pass_mode = mode;
+  return NVFP4V_OK;
+}
+
+extern "C" int nvfp4v_get_pass_mode(const nvfp4v_ctx *ctx) { return ctx ? ctx->pass_mode : NVFP4V_E_INVALID_ARG; }
+
+extern "C" int nvfp4v_last_pass_grid(const nvfp4v_ctx *ctx) { return ctx ? ctx->last_pass_grid : 0; }
+
+extern "C" int nvfp4v_pass_timeline(nvfp4v_ctx *ctx, uint64_t *out, size_t max_words, int *phases,
+                                    int *groups) {
+  if (!ctx || !out || !phases || !groups) return NVFP4V_E_INVALID_ARG;
+  if (!ctx->pass_timeline) return NVFP4V_E_INVALID_ARG;
+  const size_t n = std::min(max_words, ctx->pass_timeline_words);
+  hipError_t e = hipMemcpy(out, ctx->pass_timeline, n * sizeof(uint64_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_status(ctx, e);
+  *phases = ctx->last_pass_phases;
+  *groups = ctx->last_pass_grid;
+  return NVFP4V_OK;
+}
 
 extern "C" const char *nvfp4v_strerror(int status) {
   switch (status) {
@@ -80,6 +113,7 @@ extern "C" const char *nvfp4v_strerror(int status) {
     case NVFP4V_E_FAULT: return "injected fault (NVFP4V_FAULT=launch)";
     case NVFP4V_E_NONFINITE: return "non-finite input";
     case NVFP4V_E_WORKSPACE: return "request exceeds the context's split-K workspace";
+    case NVFP4V_E_TIMEOUT: return "a persistent pass timed out at a grid barrier";
     default: return "unknown status";
   }
 }

@@ -1,0 +1,370 @@
+// Device code of the verify GEMM, shared by the per-call kernel (gemm.hip)
+// and the persistent whole-pass kernel (pass.hip). See gemm.hip for the design.
+#pragma once
+
+#include <hip/hip_bf16.h>
+
+#include "internal.h"
+
+namespace nvfp4v {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WG_WAVES = 4;
+constexpr int WG_THREADS = 64 * WG_WAVES;
+constexpr int OOB = 0x7FFFFFF0;  // a buffer offset past every range: the load returns zeros
+constexpr int RAW_BUFFER_FLAGS = 0x00020000;
+
+template <int SEL>
+__device__ inline uint32_t dq_pair(uint32_t codes, float s) {
+  // Two E2M1 codes of byte SEL (low nibble = even k) -> fp32, times the block
+  // scale, high halves packed as bf16x2 (exact).
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, SEL);
+  const float x = v.x * s, y = v.y * s;
+  return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+}
+
+__device__ inline bf16x8 dequant8(uint32_t codes, float s) {
+  uint32_t o[4];
+  o[0] = dq_pair<0>(codes, s);
+  o[1] = dq_pair<1>(codes, s);
+  o[2] = dq_pair<2>(codes, s);
+  o[3] = dq_pair<3>(codes, s);
+  bf16x8 r;
+  __builtin_memcpy(&r, o, 16);
+  return r;
+}
+
+// The four E4M3 scale bytes of a lane -> fp32 (OCP E4M3 on gfx950, exact).
+__device__ inline void scales4(uint32_t sw, float s[4]) {
+  s[0] = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
+  s[1] = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
+  s[2] = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2);
+  s[3] = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
+}
+
+struct WTile {
+  uint4 c[2];  // code halves
+  uint32_t s;  // 4 scale bytes
+};
+
+// One row tile's k-tile (three loads per lane); `ok` false gives zeros.
+__device__ inline void load_wtile(WTile &t, __amdgpu_buffer_rsrc_t rs, int kt, bool ok, int lane) {
+  const int base = ok ? kt * TILE_BYTES : OOB;
+  const auto c0 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + lane * 16, 0, 0);
+  const auto c1 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + CODE_HALF_BYTES + lane * 16, 0, 0);
+  const auto sc = __builtin_amdgcn_raw_buffer_load_b32(rs, base + SCALE_OFFSET + lane * 4, 0, 0);
+  __builtin_memcpy(&t.c[0], &c0, 16);
+  __builtin_memcpy(&t.c[1], &c1, 16);
+  t.s = (uint32_t)sc;
+}
+
+// The 8 activation fragments of k-tile kt for each 16-row block (packed
+// activations); lanes whose row is >= M, or `ok` false, read zeros.
+template <int MB>
+__device__ inline void load_afrag(bf16x8 (&b)[MB][8], __amdgpu_buffer_rsrc_t ra, int kt, bool ok,
+                                  int M, int lane) {
+  const int col = lane & 15;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const bool v = ok && mb * 16 + col < M;
+    const int base = v ? (kt * MB + mb) * 8 * ACT_FRAG_BYTES + lane * 16 : OOB;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(ra, base + q * ACT_FRAG_BYTES, 0, 0);
+      __builtin_memcpy(&b[mb][q], &x, 16);
+    }
+  }
+}
+
+template <int MB>
+__device__ inline void compute_wtile(const WTile &t, const bf16x8 (&b)[MB][8], f32x4 (&acc)[MB]) {
+  float s[4];
+  scales4(t.s, s);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t cw[4] = {t.c[c].x, t.c[c].y, t.c[c].z, t.c[c].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 wf = dequant8(cw[j], s[2 * c + (j >> 1)]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, b[mb][4 * c + j], acc[mb], 0, 0, 0);
+    }
+  }
+}
+
+// Occupancy target (waves per SIMD) for the register allocator.
+template <int MB, int R>
+constexpr int waves_per_simd() {
+  return (MB == 1 && R <= 2) ? 3 : 2;
+}
+
+__device__ inline uint16_t bf16_bits(float x) {
+  const __hip_bfloat16 b = __float2bfloat16(x);  // round to nearest even
+  uint16_t u;
+  __builtin_memcpy(&u, &b, 2);
+  return u;
+}
+
+__device__ inline float glue_pair(float g, float u, float c) {
+#pragma clang fp contract(off)
+  const float pg = g * c;
+  const float pu = u * c;
+  return pg + pu;
+}
+
+// Four consecutive bf16 outputs (column j, j % 4 == 0) of row m: into the next
+// GEMM's packed activations and the optional row-major copies.
+__device__ inline void store_next(const Epilogue &epi, int mblocks, int m, int j, int cols,
+                                  const float (&o)[4]) {
+  const uint32_t lo = (uint32_t)bf16_bits(o[0]) | ((uint32_t)bf16_bits(o[1]) << 16);
+  const uint32_t hi = (uint32_t)bf16_bits(o[2]) | ((uint32_t)bf16_bits(o[3]) << 16);
+  const uint2 v = make_uint2(lo, hi);
+  // Write-through (system-coherent) store: a consumer on another die reads it
+  // through its own L2 without a write-back fence.
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(epi.act + act_offset(m, j, mblocks)),
+                     (uint64_t)lo | ((uint64_t)hi << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (epi.rm0) *reinterpret_cast<uint2 *>(epi.rm0 + (size_t)m * cols + j) = v;
+  if (epi.rm1) *reinterpret_cast<uint2 *>(epi.rm1 + (size_t)m * cols + j) = v;
+}
+
+// Final values of the work-group's tiles are red[w][r][mb][l] summed over the
+// first nw slots (wave order). Writes C (times ts) and the fused glue.
+template <int MB, int R>
+__device__ inline void epilogue(const f32x4 *red, int nw, int tid, int M, int N, int nrt, int rt0,
+                                float ts, float *C, const Epilogue &epi) {
+  if (epi.mode == EPI_PAIR) {
+    const int half = N / 2;
+    for (int it = tid; it < (R / 2) * MB * 64; it += WG_THREADS) {
+      const int p = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+      f32x4 vg = red[((0 * R + 2 * p) * MB + mb) * 64 + l];
+      f32x4 vu = red[((0 * R + 2 * p + 1) * MB + mb) * 64 + l];
+      for (int wv = 1; wv < nw; ++wv) {
+        vg += red[((wv * R + 2 * p) * MB + mb) * 64 + l];
+        vu += red[((wv * R + 2 * p + 1) * MB + mb) * 64 + l];
+      }
+      const int m = mb * 16 + (l & 15), rtg = rt0 + 2 * p;
+      if (m >= M || rtg + 1 >= nrt) continue;
+      const int j0 = (rtg / 2) * ROWS_PER_TILE + 4 * (l >> 4);
+      if (j0 >= half) continue;
+      vg *= ts;
+      vu *= ts;
+      if (epi.write_c) {
+        *reinterpret_cast<f32x4 *>(C + (size_t)m * N + j0) = vg;
+        *reinterpret_cast<f32x4 *>(C + (size_t)m * N + half + j0) = vu;
+      }
+      const float o[4] = {glue_pair(vg[0], vu[0], epi.c), glue_pair(vg[1], vu[1], epi.c),
+                          glue_pair(vg[2], vu[2], epi.c), glue_pair(vg[3], vu[3], epi.c)};
+      store_next(epi, MB, m, j0, half, o);
+    }
+    return;
+  }
+  for (int it = tid; it < R * MB * 64; it += WG_THREADS) {
+    const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+    f32x4 v = red[((0 * R + r) * MB + mb) * 64 + l];
+    for (int wv = 1; wv < nw; ++wv) v += red[((wv * R + r) * MB + mb) * 64 + l];
+    // lane l of a tile holds D[n = 16 rt + 4 (l / 16) + i][m = 16 mb + l % 16]
+    const int m = mb * 16 + (l & 15);
+    const int rt = rt0 + r;
+    const int n0 = rt * ROWS_PER_TILE + 4 * (l >> 4);
+    if (m >= M || rt >= nrt || n0 >= N) continue;
+    v *= ts;
+    if (epi.write_c) {
+      float *dst = C + (size_t)m * N + n0;
+      if ((N & 3) == 0) {
+        *reinterpret_cast<f32x4 *>(dst) = v;
+      } else {
+        for (int i = 0; i < 4; ++i)
+          if (n0 + i < N) dst[i] = v[i];
+      }
+    }
+    if (epi.mode == EPI_SCALE && n0 >= epi.col0 && n0 < epi.col1) {
+      const float o[4] = {v[0] * epi.c, v[1] * epi.c, v[2] * epi.c, v[3] * epi.c};
+      store_next(epi, MB, m, n0 - epi.col0, epi.col1 - epi.col0, o);
+    }
+  }
+}
+
+// Arguments of one GEMM (one phase of the pass, or one verify_gemm call).
+struct GemmArgs {
+  const uint8_t *act;  // packed activations
+  int M, act_bytes;
+  const uint8_t *W;  // packed weights
+  int N, nrt, nkt, kts_per_split, ksplit;
+  float ts;
+  float *C, *part;
+  unsigned *counters;
+  Epilogue epi;
+};
+
+// One work unit: row block `rb` (R row tiles) x k-split `ks`, by the whole
+// work-group. ABUF = 2 double-buffers the activation fragments; with ABUF = 1
+// the next k-tile's fragments are loaded after the last use of the current
+// ones (large M, where two copies do not fit in registers). `red` is the
+// work-group's LDS buffer of WG_WAVES * R * MB * 64 f32x4. Every thread of the
+// work-group calls this with the same arguments; it returns with the LDS
+// buffer free for the next unit.
+template <int MB, int R, int ABUF>
+__device__ inline void gemm_unit(const GemmArgs &g, int rb, int ks, f32x4 *red) {
+  const uint8_t *__restrict__ act = g.act;
+  const int M = g.M, act_bytes = g.act_bytes, N = g.N, nrt = g.nrt, nkt = g.nkt;
+  const uint8_t *__restrict__ W = g.W;
+  const int kts_per_split = g.kts_per_split, ksplit = g.ksplit;
+  const float ts = g.ts;
+  float *__restrict__ part = g.part;
+  unsigned *__restrict__ counters = g.counters;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
+  const int rt0 = rb * R;
+  const int kA = ks * kts_per_split;
+  const int kB = min(nkt, kA + kts_per_split);
+  const int len = kB - kA;
+  const int kbeg = kA + (len * wave) / WG_WAVES;
+  const int n = kA + (len * (wave + 1)) / WG_WAVES - kbeg;  // k-tiles of this wave
+  const int stripe_bytes = nkt * TILE_BYTES;
+
+  // One buffer resource per row tile (a row tile past the matrix has no
+  // records, so its loads return zeros), one for the packed activations.
+  __amdgpu_buffer_rsrc_t rs[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rt = rt0 + r;
+    const uint8_t *base = W + (size_t)min(rt, nrt - 1) * (size_t)stripe_bytes;
+    rs[r] = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, rt < nrt ? stripe_bytes : 0,
+                                              RAW_BUFFER_FLAGS);
+  }
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void *)act, (short)0, act_bytes, RAW_BUFFER_FLAGS);
+
+  f32x4 acc[R][MB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[r][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  WTile w[R];
+  bf16x8 a0[MB][8];
+  load_afrag<MB>(a0, ra, kbeg, n > 0, M, lane);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_wtile(w[r], rs[r], kbeg, n > 0, lane);
+  if constexpr (ABUF == 2) {
+    // Two k-tiles of weights and activations in flight: ring w / a0 holds the
+    // even k-tiles of the wave's range, w1 / a1 the odd ones; each register
+    // set is refilled two k-tiles ahead as soon as it has been consumed.
+    WTile w1[R];
+    bf16x8 a1[MB][8];
+    __builtin_amdgcn_sched_barrier(0);  // set 0 is issued before set 1
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_wtile(w1[r], rs[r], kbeg + 1, n > 1, lane);
+    load_afrag<MB>(a1, ra, kbeg + 1, n > 1, M, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    // The loop body always runs both halves, so the wait counts at its head
+    // see the same order of outstanding loads on every path; an odd k-tile
+    // left over is finished after it.
+    int i = 0;
+    for (; i + 1 < n; i += 2) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        compute_wtile<MB>(w[r], a0, acc[r]);
+        load_wtile(w[r], rs[r], kbeg + i + 2, i + 2 < n, lane);
+      }
+      load_afrag<MB>(a0, ra, kbeg + i + 2, i + 2 < n, M, lane);
+      // Keep each refill where it is: if the scheduler groups both sets'
+      // loads, the next compute waits for all of them (vmcnt 0).
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        compute_wtile<MB>(w1[r], a1, acc[r]);
+        load_wtile(w1[r], rs[r], kbeg + i + 3, i + 3 < n, lane);
+      }
+      load_afrag<MB>(a1, ra, kbeg + i + 3, i + 3 < n, M, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i < n) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) compute_wtile<MB>(w[r], a0, acc[r]);
+    }
+  } else {
+    for (int i = 0; i < n; ++i) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        compute_wtile<MB>(w[r], a0, acc[r]);
+        load_wtile(w[r], rs[r], kbeg + i + 1, i + 1 < n, lane);
+      }
+      load_afrag<MB>(a0, ra, kbeg + i + 1, i + 1 < n, M, lane);
+    }
+  }
+
+  // Sum the 4 waves' tiles in wave order (LDS), then either finish here
+  // (ksplit == 1) or exchange partial tiles with the other splits.
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
+  __syncthreads();
+
+  const int npad = nrt * ROWS_PER_TILE;
+  constexpr int ITEMS = R * MB * 64;
+  int nw = WG_WAVES;
+  if (ksplit > 1) {
+    for (int it = tid; it < ITEMS; it += WG_THREADS) {
+      const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+      f32x4 v = red[((0 * R + r) * MB + mb) * 64 + l];
+#pragma unroll
+      for (int wv = 1; wv < WG_WAVES; ++wv) v += red[((wv * R + r) * MB + mb) * 64 + l];
+      const int m = mb * 16 + (l & 15), rt = rt0 + r;
+      if (m >= M || rt >= nrt) continue;
+      float *dst = part + ((size_t)ks * M + m) * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(dst + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    // The partial stores have reached memory once this wave's counters drain.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    unsigned *s_ticket = reinterpret_cast<unsigned *>(red + WG_WAVES * R * MB * 64);
+    if (tid == 0)
+      *s_ticket = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __syncthreads();
+    const bool last = *s_ticket == (unsigned)(ksplit - 1);
+    __syncthreads();  // everyone has read the ticket before the slot is reused
+    if (!last) return;
+    // Last to arrive: sum the splits in order 0..ksplit-1 into slot 0.
+    for (int it = tid; it < ITEMS; it += WG_THREADS) {
+      const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+      const int m = mb * 16 + (l & 15), rt = rt0 + r;
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (m < M && rt < nrt) {
+        const float *src = part + (size_t)m * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int s2 = 1; s2 < ksplit; ++s2) {
+          const float *s2p = src + (size_t)s2 * M * npad;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] += __hip_atomic_load(s2p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+      }
+      red[((0 * R + r) * MB + mb) * 64 + l] = v;
+    }
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    nw = 1;
+  }
+  epilogue<MB, R>(red, nw, tid, M, N, nrt, rt0, ts, g.C, g.epi);
+  __syncthreads();  // LDS free for the next unit
+}
+
+
+// LDS bytes gemm_unit needs: the cross-wave reduction buffer plus the ticket.
+template <int MB, int R>
+constexpr size_t unit_lds_bytes() {
+  return (size_t)WG_WAVES * R * MB * 64 * sizeof(f32x4) + 16;
+}
+
+}  // namespace dev
+}  // namespace nvfp4v

@@ -52,6 +52,9 @@ struct Layout {
 // coalesced 16-byte load per lane. Rows >= M are never read.
 constexpr int ACT_FRAG_BYTES = 1024;
 
+// Words of the persistent pass's barrier block (context memory).
+constexpr int PASS_SYNC_WORDS = 1280;
+
 inline size_t act_packed_bytes(int64_t m, int64_t k) {
   const int64_t mb = (m + 15) / 16, nkt = (k + 255) / 256;
   return (size_t)nkt * (size_t)mb * 8 * ACT_FRAG_BYTES;
@@ -183,7 +186,17 @@ struct nvfp4v_ctx {
   size_t n_counters = 0;
   uint8_t *act = nullptr;  // packed activations for nvfp4v_verify_gemm
   size_t act_bytes = 0;
+  unsigned *pass_sync = nullptr;  // persistent pass: barrier arrivals, finished groups, error flag
+  int pass_mode = NVFP4V_PASS_CHAIN;
+  int last_pass_grid = 0;         // work-groups of the last persistent pass launch
+  uint64_t *pass_timeline = nullptr;  // optional (NVFP4V_PASS_TRACE=1): per phase and work-group,
+                                      // real-time clock at phase start and at work done
+  size_t pass_timeline_words = 0;
+  int last_pass_phases = 0;
 };
+
+// Timeline capacity: 2 stamps for each of up to 1024 work-groups and 512 phases.
+constexpr size_t PASS_TIMELINE_WGS = 1024, PASS_TIMELINE_PHASES = 512;
 
 namespace nvfp4v {
 int fault_injected();  // NVFP4V_FAULT=launch
@@ -192,7 +205,7 @@ bool aligned16(const void *p);
 int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p);
 // Enqueue A (row-major bf16) -> packed activations (no argument checks).
 int launch_pack_act(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
-                    hipStream_t stream);
+                    hipStream_t stream, unsigned *sync = nullptr);
 // Fused epilogue of a GEMM in the chained pass: besides (optionally) writing
 // the fp32 C, turn C into the next GEMM's bf16 input, in packed-activation
 // order, and optionally into up to two row-major bf16 copies.

@@ -95,16 +95,29 @@ def manual_chain(torch, ctx, packed, h0, H, I):
     return outs
 
 
+MODES = [pytest.param(nv.PASS_CHAIN, id="chain"), pytest.param(nv.PASS_PERSISTENT, id="persistent")]
+
+
+@pytest.fixture
+def mode_ctx(ctx, request):
+    ctx.set_pass_mode(request.param)
+    yield ctx
+    ctx.set_pass_mode(nv.PASS_CHAIN)
+
+
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
 @pytest.mark.parametrize("m", [1, 8, 16, 33, 64])
-def test_pass_equals_composition(torch_cuda, ctx, m):
-    torch = torch_cuda
+def test_pass_equals_composition(torch_cuda, mode_ctx, m):
+    torch, ctx = torch_cuda, mode_ctx
     H, I, L = 256, 512, 3
     packed, arr = small_stack(torch, ctx, L, H, I)
     h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=3).view(np.int16)).cuda().view(torch.bfloat16)
-    ws = torch.empty(nv.pass_workspace_bytes(m, H, I), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
     h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
     trace = torch.empty((L, m, H), dtype=torch.bfloat16, device="cuda")
     ctx.verify_pass(arr, H, I, h0[:m], ws, h_out, trace=trace)
+    assert ctx.pass_status() == nv.OK
+    log("pass mode %d, grid %d work-groups" % (ctx.get_pass_mode(), ctx.last_pass_grid()))
     ref = manual_chain(torch, ctx, packed, h0[:m], H, I)
     for l in range(L):
         assert torch.equal(trace[l].view(torch.int16), ref[l].view(torch.int16)), "layer %d" % l
@@ -122,12 +135,32 @@ def test_pass_equals_composition(torch_cuda, ctx, m):
     assert torch.equal(outs[0].view(m, 3 * H), qkv)
 
 
-def test_graph_replays_equal_eager(torch_cuda, ctx):
-    torch = torch_cuda
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
+def test_pass_longer_than_one_launch(torch_cuda, mode_ctx):
+    """40 layers: the persistent kernel runs 32 layers per launch, so the chain
+    crosses a launch boundary; still bitwise the composition of single calls."""
+    torch, ctx = torch_cuda, mode_ctx
+    H, I, L, m = 256, 512, 40, 16
+    packed, arr = small_stack(torch, ctx, L, H, I, seed=9)
+    h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=8).view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
+    h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    trace = torch.empty((L, m, H), dtype=torch.bfloat16, device="cuda")
+    ctx.verify_pass(arr, H, I, h0[:m], ws, h_out, trace=trace)
+    assert ctx.pass_status() == nv.OK
+    ref = manual_chain(torch, ctx, packed, h0[:m], H, I)
+    for l in range(L):
+        assert torch.equal(trace[l].view(torch.int16), ref[l].view(torch.int16)), "layer %d" % l
+    assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16))
+
+
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
+def test_graph_replays_equal_eager(torch_cuda, mode_ctx):
+    torch, ctx = torch_cuda, mode_ctx
     H, I, L, m = 512, 1024, 4, 16
     packed, arr = small_stack(torch, ctx, L, H, I, seed=1)
     h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=4).view(np.int16)).cuda().view(torch.bfloat16)
-    ws = torch.empty(nv.pass_workspace_bytes(m, H, I), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
     eager = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
     ctx.verify_pass(arr, H, I, h0[:m], ws, eager)
     torch.cuda.synchronize()
@@ -150,40 +183,111 @@ def test_graph_replays_equal_eager(torch_cuda, ctx):
         torch.cuda.synchronize()
 
 
-def test_full_size_layer0_against_oracle(torch_cuda, ctx, oracle_mod):
-    """One layer of the full-size stack through the pass (M = 16): its q|k|v outputs,
-    whose input comes from the generator, are checked against the oracle on 1536
-    sampled weight rows."""
-    torch = torch_cuda
-    H, I, m = 5120, 17408, 16
-    log("full-size layer 0")
-    packed, arr = small_stack(torch, ctx, 1, H, I, seed=2)
-    a = synth.activations_bf16(64, H, seed=0, stream="pass/h0")
-    h0 = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-    ws = torch.empty(nv.pass_workspace_bytes(m, H, I), dtype=torch.uint8, device="cuda")
+def align256(x):
+    return (x + 255) // 256 * 256
+
+
+def act_packed_bytes(m, k):
+    return ((k + 255) // 256) * ((m + 15) // 16) * 8 * 1024
+
+
+def unpack_act(buf, m, k):
+    """Packed activations (the layout the GEMM kernels read) -> bf16 bits [m, k]."""
+    mb = (m + 15) // 16
+    rows = np.arange(m)[:, None]
+    ks = np.arange(k)[None, :]
+    kt, rem = ks >> 8, ks & 255
+    h, q, e = rem >> 6, (rem >> 3) & 7, rem & 7
+    off = ((kt * mb + (rows >> 4)) * 8 + q) * 1024 + ((rows & 15) + 16 * h) * 16 + 2 * e
+    return buf.view(np.uint16)[off // 2]
+
+
+def workspace_views(ws, m, H, I, L):
+    """fp32 outputs of the last layer and each layer's packed input blocks."""
+    sizes = [m * 3 * H * 4, m * H * 4, m * 2 * I * 4, m * H * 4]
+    C, off = [], 0
+    for sz in sizes:
+        C.append(ws[off:off + sz].view(np.float32))
+        off += align256(sz)
+    act_bytes = [act_packed_bytes(m, H)] * 3 + [act_packed_bytes(m, I)]
+    stride = sum(align256(b) for b in act_bytes)
+    acts = []
+    for l in range(L + 1):
+        blk, o = [], off + l * stride
+        for b in act_bytes:
+            blk.append(ws[o:o + b])
+            o += align256(b)
+        acts.append(blk)
+    return C, acts
+
+
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
+@pytest.mark.parametrize("m", [16, 24])
+def test_full_size_phases_against_oracle(torch_cuda, mode_ctx, oracle_mod, m):
+    """Two full-size layers (H = 5120, I = 17408). For the last layer, every
+    GEMM's fp32 output is checked against the oracle on 384 sampled weight
+    rows, fed with the packed activations the kernels read, taken back from
+    the workspace; every glue step (and the hand-over between layers) is
+    checked bitwise against the oracle's glue on the fp32 outputs."""
+    torch, ctx = torch_cuda, mode_ctx
+    H, I, L = 5120, 17408, 2
+    log("full-size pass, mode %d, M = %d" % (ctx.get_pass_mode(), m))
+    packed, arr = small_stack(torch, ctx, L, H, I, seed=2)
+    a0 = synth.activations_bf16(64, H, seed=0, stream="pass/h0")
+    h0 = torch.from_numpy(a0.view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
     h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
-    ctx.verify_pass(arr, H, I, h0[:m], ws, h_out)
+    trace = torch.empty((L, m, H), dtype=torch.bfloat16, device="cuda")
+    ctx.verify_pass(arr, H, I, h0[:m], ws, h_out, trace=trace)
+    assert ctx.pass_status() == nv.OK
     torch.cuda.synchronize()
-    qkv = ws[: m * 3 * H * 4].view(torch.float32).view(m, 3 * H).cpu().numpy()
-    rows = np.sort(np.random.default_rng(5).choice(3 * H, 1536, replace=False))
-    w = torch.cat([synth.weights_f32_cuda(H, H, seed=2, stream="t0/%s" % p) for p in ("q", "k", "v")])
-    w_rows = w[torch.from_numpy(rows).cuda()].cpu().numpy()
-    del w
-    oc, osc = oracle_mod.quantize(w_rows)
-    c_ref, s_ref = oracle_mod.gemm(a[:m], oc, osc)
-    ok = oracle_mod.within_tolerance(qkv[:, rows], c_ref, s_ref)
-    assert ok.all(), "%d of %d sampled qkv outputs outside 1e-5*S" % ((~ok).sum(), ok.size)
+    C, acts = workspace_views(ws.cpu().numpy(), m, H, I, L)
+    last = L - 1
+    h_in = unpack_act(acts[last][0], m, H)
+    assert np.array_equal(unpack_act(acts[0][0], m, H), a0[:m].view(np.uint16))
+    assert np.array_equal(h_in, trace[last - 1].view(torch.int16).cpu().numpy().view(np.uint16))
+    ins = [h_in, unpack_act(acts[last][1], m, H), unpack_act(acts[last][2], m, H),
+           unpack_act(acts[last][3], m, I)]
+    outs = [C[0].reshape(m, 3 * H), C[1].reshape(m, H), C[2].reshape(m, 2 * I), C[3].reshape(m, H)]
+    # glue: o_in, g_in, d_in and the layer's output h
+    c_h, c_i, c_2 = f32(1 / math.sqrt(H)), f32(1 / math.sqrt(I)), f32(1 / math.sqrt(2 * H))
+    assert np.array_equal(ins[1], oracle_mod.glue_scale(np.ascontiguousarray(outs[0][:, 2 * H:]), c_h))
+    assert np.array_equal(ins[2], oracle_mod.glue_scale(outs[1], c_h))
+    assert np.array_equal(ins[3], oracle_mod.glue_sum(np.ascontiguousarray(outs[2][:, :I]),
+                                                      np.ascontiguousarray(outs[2][:, I:]), c_2))
+    hq = h_out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(hq, oracle_mod.glue_scale(outs[3], c_i))
+    # GEMMs: sampled rows of each projection against the oracle
+    rng = np.random.default_rng(17)
+    mats = [("qkv", ("q", "k", "v"), H, H), ("o", ("o",), H, H), ("gate_up", ("gate", "up"), I, H),
+            ("down", ("down",), H, I)]
+    for j, (name, parts, n_part, k) in enumerate(mats):
+        n = n_part * len(parts)
+        rows = np.sort(rng.choice(n, 384, replace=False))
+        w_rows = np.empty((len(rows), k), np.float32)
+        for pi, part in enumerate(parts):
+            sel = (rows // n_part) == pi
+            if not sel.any():
+                continue
+            w = synth.weights_f32_cuda(n_part, k, seed=2, stream="t%d/%s" % (last, part))
+            w_rows[sel] = w[torch.from_numpy(rows[sel] % n_part).cuda()].cpu().numpy()
+            del w
+        oc, osc = oracle_mod.quantize(w_rows)
+        c_ref, s_ref = oracle_mod.gemm(ins[j], oc, osc)
+        ok = oracle_mod.within_tolerance(outs[j][:, rows], c_ref, s_ref)
+        assert ok.all(), "%s: %d of %d sampled outputs outside 1e-5*S" % (name, (~ok).sum(), ok.size)
 
 
-def test_full_stack_stays_finite_and_bounded(torch_cuda, ctx):
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
+def test_full_stack_stays_finite_and_bounded(torch_cuda, mode_ctx):
     """64 layers at full size, M = 16: the linear glue keeps the RMS O(1)."""
-    torch = torch_cuda
+    torch, ctx = torch_cuda, mode_ctx
     H, I, L, m = 5120, 17408, 64, 16
     log("building 64-layer stack")
     packed, arr = small_stack(torch, ctx, L, H, I, seed=7)
     h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=0, stream="pass/h0").view(np.int16)).cuda()
     h0 = h0.view(torch.bfloat16)
-    ws = torch.empty(nv.pass_workspace_bytes(m, H, I), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
     h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
     trace = torch.empty((L, m, H), dtype=torch.bfloat16, device="cuda")
     ctx.verify_pass(arr, H, I, h0[:m], ws, h_out, trace=trace)
