@@ -8,10 +8,12 @@ to layer. One step = one pass, replayed from a HIP graph; weights and inputs are
 resident in HBM before the timed region.
 
 Prints one JSON line: value = achieved HBM GB/s of the pass at M = --m
-(weight + scale bytes / pass time), plus the per-M staircase of the pass
-(M = 1..32), a roofline entry for the dominant kernel (the verify GEMM) from
-HIP events on its own stream, the HBM read ceiling measured by a plain
-streaming kernel, and the CPU oracle timed on the host's cores over a bounded
+(weight + scale bytes / pass time) in the chosen schedule (the other schedule's
+time beside it), the per-M staircase of the pass (M = 1..32), a roofline entry
+for the dominant kernel (the verify GEMM, timed alone with HIP events on its
+own stream), the HBM read ceiling measured by a plain streaming kernel, the
+per-shape GEMM staircase M = 1..64 with its step positions (LM head and the
+layer shapes), and the CPU oracle timed on the host's cores over a bounded
 sample of the same GEMMs.
 """
 
@@ -117,44 +119,48 @@ def capture_pass(torch, ctx, layer_arr, h0, ws, h_out, m):
     return g
 
 
-def gemm_event_timing(torch, ctx, packed, h0, m, passes=2):
-    """Run the pass eagerly, op by op, with HIP events around every GEMM launch on
-    the stream the GEMMs run on. Returns (sum of GEMM bytes, sum of GEMM ms, launches)."""
-    stream = torch.cuda.current_stream()
-    c_h = float((1.0 / (H ** 0.5)))
-    c_i = float((1.0 / (I ** 0.5)))
-    c_2 = float((1.0 / ((2 * H) ** 0.5)))
-    qkv = torch.empty((m, 3 * H), dtype=torch.float32, device="cuda")
-    o = torch.empty((m, H), dtype=torch.float32, device="cuda")
-    gu = torch.empty((m, 2 * I), dtype=torch.float32, device="cuda")
-    d = torch.empty((m, H), dtype=torch.float32, device="cuda")
-    events = []
-    total_bytes = 0
-    for _ in range(passes):
-        h = h0[:m]
-        for mats in packed:
-            for (a, name, n, k, out) in (("h", "qkv", 3 * H, H, qkv), ("o_in", "o", H, H, o),
-                                         ("g_in", "gate_up", 2 * I, H, gu), ("d_in", "down", H, I, d)):
-                if name == "o":
-                    a_t = ctx.glue_scale(qkv[:, 2 * H:], c_h)
-                elif name == "gate_up":
-                    a_t = ctx.glue_scale(o, c_h)
-                elif name == "down":
-                    t = gu.view(m, I // 16, 2, 16)
-                    a_t = ctx.glue_sum(t[:, :, 0].reshape(m, I), t[:, :, 1].reshape(m, I), c_2)
-                else:
-                    a_t = h
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                ctx.verify_gemm(a_t, mats[name], n, k, out=out)
-                e1.record(stream)
-                events.append((e0, e1))
-                total_bytes += int(n * k * BYTES_PER_WEIGHT)
-            h = ctx.glue_scale(d, c_i)
+def gemm_event_timing(torch, ctx, packed, m, reps=2):
+    """The verify GEMM kernel alone, as the pass launches it at M = m: activations
+    packed once per shape (pack_activations), then one verify_gemm_pa launch per
+    layer and projection, timed with HIP events on the stream the kernel runs on
+    (one pair around each shape's 64 back-to-back launches). Returns (algorithmic
+    weight+scale bytes, summed ms, launches, per-shape {us, GBps, plan})."""
+    import synth
+
+    stream = torch.cuda.current_stream()  # the stream verify_gemm_pa launches on
+    shapes = (("qkv", 3 * H, H), ("o", H, H), ("gate_up", 2 * I, H), ("down", H, I))
+    acts = {}
+    for name, n, k in shapes:
+        a = torch.from_numpy(synth.activations_bf16(64, k, seed=0, stream="roofline/%d" % k)[:m].view("int16"))
+        acts[k] = ctx.pack_activations(a.cuda().view(torch.bfloat16))
+    outs = {name: torch.empty((m, n), dtype=torch.float32, device="cuda") for name, n, k in shapes}
+    for name, n, k in shapes:  # warm-up
+        ctx.verify_gemm_pa(acts[k], m, k, packed[0][name], n, out=outs[name])
     torch.cuda.synchronize()
-    total_ms = sum(e0.elapsed_time(e1) for e0, e1 in events)
-    return total_bytes, total_ms, len(events)
+    # One event pair around each shape's back-to-back launches (all layers):
+    # per-launch pairs would add the dispatch latency of every launch.
+    events = {name: [] for name, _, _ in shapes}
+    for _ in range(reps):
+        for name, n, k in shapes:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for mats in packed:
+                ctx.verify_gemm_pa(acts[k], m, k, mats[name], n, out=outs[name])
+            e1.record(stream)
+            events[name].append((e0, e1, len(packed)))
+    torch.cuda.synchronize()
+    total_bytes, total_ms, launches, per_shape = 0, 0.0, 0, {}
+    for name, n, k in shapes:
+        ms = sum(e0.elapsed_time(e1) for e0, e1, _ in events[name])
+        cnt = sum(c for _, _, c in events[name])
+        b = int(n * k * BYTES_PER_WEIGHT)
+        per_shape[name] = {"us": round(1e3 * ms / cnt, 2), "GBps": round(b * cnt / (ms * 1e-3) / 1e9, 1),
+                           "plan": ctx.describe_plan(n, k, m)}
+        total_bytes += b * cnt
+        total_ms += ms
+        launches += cnt
+    return total_bytes, total_ms, launches, per_shape
 
 
 def read_ceiling(torch, ctx, gib=4, reps=5):
@@ -177,9 +183,11 @@ def read_ceiling(torch, ctx, gib=4, reps=5):
     return (gib << 30) / (t[len(t) // 2] * 1e-3) / 1e9
 
 
-def cpu_baseline(target_s=12.0, m=16):
-    """The oracle (as it stands) on the host cores: decode + fp64 GEMM over a
-    bounded sample of the pass's weight rows (all four projection shapes)."""
+def cpu_baseline(target_s=12.0, m=16, rows=512):
+    """The oracle (as it stands) on the host's cores: decode + fp64 GEMM of an
+    M = m activation block against the first `rows` weight rows of each of the
+    pass's four projection shapes, repeated until about target_s seconds of
+    GEMM time (input generation and quantisation are not timed)."""
     import numpy as np
 
     import oracle
@@ -189,29 +197,34 @@ def cpu_baseline(target_s=12.0, m=16):
     threads = oracle.thread_count()
     a_h = synth.activations_bf16(m, H, seed=0, stream="cpu/h")
     a_i = synth.activations_bf16(m, I, seed=0, stream="cpu/i")
-    shapes = [("qkv", 3 * H, H, a_h), ("o", H, H, a_h), ("gate_up", 2 * I, H, a_h), ("down", H, I, a_i)]
-    # calibrate on a small sample, then size the real one to about target_s seconds
-    w = synth.weights_f32(256, H, seed=0, stream="cpu/cal")
-    codes, scales = oracle.quantize(w)
-    t0 = time.perf_counter()
-    oracle.gemm(a_h, codes, scales)
-    rate = 256 * H / max(time.perf_counter() - t0, 1e-6)  # weights per second
-    per_shape_weights = rate * target_s / len(shapes)
-    total_w, total_t = 0, 0.0
-    desc = []
-    for name, n, k, a in shapes:
-        rows = int(max(1, min(n, per_shape_weights / k)))
+    work = []
+    for name, n, k, a in (("qkv", 3 * H, H, a_h), ("o", H, H, a_h), ("gate_up", 2 * I, H, a_h),
+                          ("down", H, I, a_i)):
         w = synth.weights_f32(n, k, seed=0, stream="cpu/" + name, rows=np.arange(rows))
         codes, scales = oracle.quantize(w)
-        t0 = time.perf_counter()
-        oracle.gemm(a, codes, scales, threads=threads)
-        total_t += time.perf_counter() - t0
-        total_w += rows * k
-        desc.append("%s %dx%d" % (name, rows, k))
+        work.append((a, codes, scales, rows * k))
+    total_w, total_t, reps = 0, 0.0, 0
+    while total_t < target_s:
+        for a, codes, scales, nw in work:
+            t0 = time.perf_counter()
+            oracle.gemm(a, codes, scales, threads=threads)
+            total_t += time.perf_counter() - t0
+            total_w += nw
+        reps += 1
     gbs = total_w * BYTES_PER_WEIGHT / total_t / 1e9
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "oracle decode + fp64 GEMM at M=%d over the first rows of each projection "
-                      "shape (%s), %.1f s" % (m, ", ".join(desc), total_t)}
+            "sample": "oracle decode + fp64 GEMM at M=%d of the first %d weight rows of each projection "
+                      "(q|k|v 15360x5120, o 5120x5120, gate|up 34816x5120, down 5120x17408), %d "
+                      "repetitions, %.1f s; weight+scale bytes per second" % (m, rows, reps, total_t)}
+
+
+def kernel_source_hash():
+    """sha256 over the verify GEMM's device sources (the traffic figure in
+    profiles/ is valid only for the kernel it was taken on)."""
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "gemm_device.h"):
+        h.update(open(os.path.join(ROOT, "nvfp4_skinny_gemm_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def traffic_from_profile(gemm_src_hash):
@@ -246,16 +259,51 @@ def parse_sweep(s):
     return out
 
 
+def find_steps(us, m0=1):
+    """Staircase steps: M where the time exceeds 1.03x the median of the plateau
+    of preceding M values by more than 3 MADs of that plateau's noise."""
+    import numpy as np
+
+    steps, start = [], 0
+    for i in range(1, len(us)):
+        plateau = np.asarray(us[start:i])
+        med = float(np.median(plateau))
+        mad = float(np.median(np.abs(plateau - med))) if len(plateau) > 1 else 0.0
+        if us[i] > 1.03 * med and us[i] - med > 3 * mad:
+            steps.append(m0 + i)
+            start = i
+    return steps
+
+
+def staircase_report(ctx, m_hi=64, reps=7):
+    """A10: microseconds per M (1..m_hi) of the verify GEMM on the LM head and
+    the layer shapes (rotating >= 2 GiB of weight copies), with step positions."""
+    shapes = (("head", 151936, 5120), ("qkvo", 5120, 5120), ("gate_up", 17408, 5120), ("down", 5120, 17408))
+    out = {}
+    for name, n, k in shapes:
+        us = [round(float(x), 2) for x in ctx.staircase(n, k, 1, m_hi, warmup=2, reps=reps, rotate_bytes=2 << 30)]
+        out[name] = {"shape": [n, k], "us": us, "steps": find_steps(us),
+                     "GBps_m16": round(n * k * BYTES_PER_WEIGHT / (us[15] * 1e-6) / 1e9, 1)}
+        log("staircase %s [%dx%d]: M1 %.1f us, M16 %.1f, M32 %.1f, M64 %.1f; steps at %s" % (
+            name, n, k, us[0], us[15], us[31], us[63], out[name]["steps"]))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--m", type=int, default=16)
+    ap.add_argument("--mode", choices=("chain", "persistent"), default="chain",
+                    help="pass schedule of the headline number (the other is reported beside it)")
     ap.add_argument("--sweep", default="1-32", help="M values for the per-M pass staircase ('' = none)")
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-staircase", action="store_true")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="only the verify-GEMM roofline leg and a 256 MiB copy (for hardware-counter runs)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -273,6 +321,21 @@ def main():
     layers = args.layers
     log("device: %s, %d layers" % (torch.cuda.get_device_name(0), layers))
     packed = build_stack(torch, nv, synth, ctx, layers)
+
+    if args.gemm_only:
+        gbytes, gms, launches, per_shape = gemm_event_timing(torch, ctx, packed, args.m)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        src.fill_(3)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        ctx.copy_probe(src, dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"gemm_launches": launches, "algorithmic_bytes_per_launch": gbytes / launches,
+                          "avg_launch_us": gms * 1e3 / launches, "copy_probe_bytes": 256 << 20,
+                          "per_shape": per_shape}), flush=True)
+        ctx.close()
+        return
+
     layer_arr = (nv.Layer * layers)()
     for l, mats in enumerate(packed):
         layer_arr[l] = nv.Layer(mats["qkv"].data_ptr(), mats["o"].data_ptr(),
@@ -282,52 +345,59 @@ def main():
     ws = torch.empty(nv.pass_workspace_bytes(64, H, I, layers), dtype=torch.uint8, device="cuda")
     h_out = torch.empty((64, H), dtype=torch.bfloat16, device="cuda")
     pass_bytes = layer_weight_bytes() * layers
+    modes = {"chain": nv.PASS_CHAIN, "persistent": nv.PASS_PERSISTENT}
+    other = "persistent" if args.mode == "chain" else "chain"
+
+    def timed_pass(m, warmup, steps):
+        launch = "graph"
+        try:
+            runner = capture_pass(torch, ctx, layer_arr, h0, ws, h_out, m)
+        except Exception as exc:  # the runtime cannot capture this schedule
+            log("graph capture unavailable (%s); timing direct launches" % type(exc).__name__)
+            launch = "direct"
+            runner = DirectPass(torch, ctx, layer_arr, h0, ws, h_out, m)
+        sec = time_graph(torch, runner, warmup, steps)
+        assert ctx.pass_status() == nv.OK, "persistent pass timed out"
+        del runner
+        return sec, launch
 
     # ---- headline: the pass at M = args.m --------------------------------------
-    # A pass is one packing kernel plus the layers' GEMM launches (or one
-    # persistent kernel per 32 layers); it is replayed from a HIP graph when the
-    # runtime can capture it, else enqueued directly.
-    mode = "graph"
-    try:
-        runner = capture_pass(torch, ctx, layer_arr, h0, ws, h_out, args.m)
-    except Exception as exc:  # capture of cooperative launches unsupported
-        log("graph capture unavailable (%s); timing direct launches" % type(exc).__name__)
-        mode = "direct"
-        runner = DirectPass(torch, ctx, layer_arr, h0, ws, h_out, args.m)
-    sec = time_graph(torch, runner, args.warmup, args.steps)
-    assert ctx.pass_status() == nv.OK, "persistent pass timed out"
+    # One step is one pass over all layers: a packing kernel plus the layers'
+    # GEMMs (four launches per layer, or one persistent kernel per 32 layers),
+    # replayed from a HIP graph; weights and input are resident in HBM.
+    ctx.set_pass_mode(modes[other])
+    sec_other, _ = timed_pass(args.m, 2, max(3, args.steps // 4))
+    ctx.set_pass_mode(modes[args.mode])
+    sec, launch = timed_pass(args.m, args.warmup, args.steps)
     assert torch.isfinite(h_out[: args.m].float()).all(), "non-finite pass output"
     gbs = pass_bytes / sec / 1e9
-    log("M=%d: %.1f us per pass, %.1f GB/s (%s, grid %d)" % (args.m, sec * 1e6, gbs, mode,
-                                                             ctx.last_pass_grid()))
-    del runner
+    log("M=%d: %.1f us per pass, %.1f GB/s (%s, %s); %s schedule %.1f us" % (
+        args.m, sec * 1e6, gbs, args.mode, launch, other, sec_other * 1e6))
 
     # ---- per-M staircase of the pass ------------------------------------------
     per_m = {}
     for m in parse_sweep(args.sweep):
-        gm = (capture_pass(torch, ctx, layer_arr, h0, ws, h_out, m) if mode == "graph"
-              else DirectPass(torch, ctx, layer_arr, h0, ws, h_out, m))
-        s = time_graph(torch, gm, 2, args.sweep_steps)
-        per_m[str(m)] = {"us": round(s * 1e6, 1), "GBps": round(pass_bytes / s / 1e9, 1),
-                         "TFLOPs": round(2.0 * m * pass_bytes / BYTES_PER_WEIGHT / s / 1e12, 2)}
-        del gm
+        s_m, _ = timed_pass(m, 2, args.sweep_steps)
+        per_m[str(m)] = {"us": round(s_m * 1e6, 1), "GBps": round(pass_bytes / s_m / 1e9, 1),
+                         "TFLOPs": round(2.0 * m * pass_bytes / BYTES_PER_WEIGHT / s_m / 1e12, 2)}
     if per_m:
-        log("staircase: " + " ".join("%s:%.0f" % (k, v["us"]) for k, v in per_m.items()))
+        log("pass staircase: " + " ".join("%s:%.0f" % (k, v["us"]) for k, v in per_m.items()))
 
-    # ---- roofline of the dominant kernel (verify GEMM), HIP events -------------
-    gbytes, gms, launches = gemm_event_timing(torch, ctx, packed, h0, args.m)
+    # ---- roofline of the dominant kernel (the verify GEMM), HIP events ----------
+    gbytes, gms, launches, per_shape = gemm_event_timing(torch, ctx, packed, args.m)
     achieved = gbytes / (gms * 1e-3) / 1e9
-    src_hash = hashlib.sha256(open(os.path.join(ROOT, "nvfp4_skinny_gemm_amd", "csrc", "gemm.hip"),
-                                   "rb").read()).hexdigest()
-    traffic = traffic_from_profile(src_hash)
+    traffic = traffic_from_profile(kernel_source_hash())
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": "k_gemm_mfma (verify GEMM), M=%d" % args.m,
+                "kernel": "k_gemm (verify GEMM) at M=%d over the pass's four projection shapes" % args.m,
                 "avg_launch_us": round(gms * 1e3 / launches, 2),
-                "algorithmic_bytes_per_launch": round(gbytes / launches)}
+                "algorithmic_bytes_per_launch": round(gbytes / launches), "launches": launches,
+                "per_shape": per_shape}
     ceiling = read_ceiling(torch, ctx)
-    log("GEMM kernels alone: %.1f GB/s (%.1f%% of peak); read ceiling %.1f GB/s" % (
+    log("GEMM kernel alone: %.1f GB/s (%.1f%% of peak); read ceiling %.1f GB/s" % (
         achieved, 100 * achieved / PEAK_HBM_GBS, ceiling))
+
+    stair = None if args.no_staircase else staircase_report(ctx)
 
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
@@ -337,14 +407,14 @@ def main():
         "config": {"workload": "full verify pass: %d layers x (q,k,v,o 5120x5120; gate,up 17408x5120; "
                                "down 5120x17408) NVFP4, M=%d bf16 rows" % (layers, args.m),
                    "m": args.m, "layers": layers, "weight_bytes_per_pass": pass_bytes,
-                   "launch": "%s, %s" % ("4 GEMM launches per layer" if ctx.get_pass_mode() == nv.PASS_CHAIN
-                                         else "persistent kernel per 32 layers", mode),
-                   "grid": ctx.last_pass_grid()},
+                   "schedule": args.mode, "launch": launch},
         "pass_us": round(sec * 1e6, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "pass_us_%s" % other: round(sec_other * 1e6, 1),
         "per_m": per_m,
         "roofline": roofline,
         "read_ceiling_GBps": round(ceiling, 1),
+        "staircase": stair,
         "pages_context": PAGES_CONTEXT,
     }
     if not args.no_cpu_baseline:

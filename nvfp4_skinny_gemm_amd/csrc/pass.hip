@@ -226,16 +226,24 @@ struct Item {
 };
 
 // The task's pieces and piece index (q = 1: a whole row block).
-__device__ inline void task_split(const PhaseShape &ps, const Item &it, int g, int *q, int *s) {
-  if (it.task < ps.full) {
-    *q = 1, *s = 0;
-  } else {
-    *q = ps.q, *s = g % ps.q;
-  }
-}
-
 __device__ inline int task_count(const PhaseShape &ps, int g, int G) {
   return ps.full + (g < ps.rem * ps.q ? 1 : 0);
+}
+
+// Task order within a phase: the K-split piece (if the work-group has one)
+// first, so that its slower flush overlaps the streaming of the whole row
+// blocks instead of delaying the phase's end; then the whole row blocks.
+__device__ inline bool task_is_piece(const PhaseShape &ps, int task, int g) {
+  return task == 0 && g < ps.rem * ps.q;
+}
+
+// The task's pieces and piece index (q = 1: a whole row block).
+__device__ inline void task_split(const PhaseShape &ps, const Item &it, int g, int *q, int *s) {
+  if (task_is_piece(ps, it.task, g)) {
+    *q = ps.q, *s = g % ps.q;
+  } else {
+    *q = 1, *s = 0;
+  }
 }
 
 // Point `it` at the first item of task it.task of phase it.p, moving on to the
@@ -245,13 +253,14 @@ __device__ inline void seek(Item &it, const PassArgs &a, int np, int g, int G, i
     const PhaseShape &ps = a.ph[it.p & 3];
     if (it.task < task_count(ps, g, G)) {
       int ka = 0, kb = ps.nkt;
-      if (it.task < ps.full) {
-        it.rb = g + G * it.task;
-      } else {
+      if (task_is_piece(ps, it.task, g)) {
         const int s = g % ps.q;
         it.rb = ps.full * G + g / ps.q;
         ka = (int)((int64_t)ps.nkt * s / ps.q);
         kb = (int)((int64_t)ps.nkt * (s + 1) / ps.q);
+      } else {
+        const int unit = it.task - (g < ps.rem * ps.q ? 1 : 0);
+        it.rb = g + G * unit;
       }
       const int len = kb - ka;
       it.kt = ka + (len * wave) / WG_WAVES;
