@@ -53,7 +53,35 @@ void k_gemm(GemmArgs g) {
   gemm_unit<MB, R, ABUF>(g, blockIdx.x, blockIdx.y, red);
 }
 
+template <int MB, int R>
+constexpr int lds_waves_per_simd() {
+  return MB == 1 ? (R == 1 ? 4 : 3) : 2;
+}
+
+template <int MB, int R>
+__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(lds_waves_per_simd<MB, R>())))
+void k_gemm_lds(GemmArgs g) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  gemm_unit_lds<MB, R>(g, blockIdx.x, blockIdx.y, lds);
+}
+
 typedef void (*GemmKernel)(GemmArgs);
+
+GemmKernel pick_lds_kernel(int mb, int r) {
+  switch (mb * 16 + r) {
+    case 1 * 16 + 1: return k_gemm_lds<1, 1>;
+    case 1 * 16 + 2: return k_gemm_lds<1, 2>;
+    case 2 * 16 + 1: return k_gemm_lds<2, 1>;
+    case 2 * 16 + 2: return k_gemm_lds<2, 2>;
+    case 3 * 16 + 1: return k_gemm_lds<3, 1>;
+    case 4 * 16 + 1: return k_gemm_lds<4, 1>;
+    default: return nullptr;
+  }
+}
+
+size_t lds_variant_bytes(int mb, int r) {
+  return (size_t)2 * mb * 8 * ACT_FRAG_BYTES + (size_t)WG_WAVES * r * mb * 64 * sizeof(f32x4) + 16;
+}
 
 GemmKernel pick_kernel(int mb, int r) {
   switch (mb * 16 + r) {
@@ -124,24 +152,41 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
   else
     p->rb = nrt >= 640 ? 4 : 2;
   int want_ks = (nkt >= 48 && nrt <= 640) ? 3 : 1;
+  p->lds = 0;
+  // Activations staged in LDS (waves split N) where the N tile is wide enough
+  // to give every CU work without a k-split: the LM head up to 32 rows, and the
+  // 2.5k-9k-row projections at 17..32 rows, where the register-only variant's
+  // per-wave fragment reloads cost the most (measured on MI355X).
+  if (p->mblocks <= 2 && nrt >= 4096) {
+    p->lds = 1, p->rb = 2, want_ks = 1;
+  } else if (p->mblocks == 2 && nrt >= 640 && nkt < 48) {
+    p->lds = 1, p->rb = 1, want_ks = 1;
+  }
   if (const char *ov = std::getenv("NVFP4V_PLAN")) {
     int r = 0, k2 = 0;
-    if (std::sscanf(ov, "r=%d,ks=%d", &r, &k2) == 2 && (r == 1 || r == 2 || r == 4 || r == 8)) {
+    if (std::sscanf(ov, "n:r=%d,ks=%d", &r, &k2) == 2 && pick_lds_kernel(p->mblocks, r)) {
+      p->lds = 1;
+      p->rb = r;
+      want_ks = k2 > 0 ? k2 : 1;
+    } else if (std::sscanf(ov, "r=%d,ks=%d", &r, &k2) == 2 && (r == 1 || r == 2 || r == 4 || r == 8)) {
+      p->lds = 0;
       p->rb = r;
       want_ks = k2 > 0 ? k2 : 1;
     }
   }
   (void)ctx;
   int force_ks = want_ks;
-  if (!pick_kernel(p->mblocks, p->rb)) p->rb = 4;
-  p->grid_x = (int)((L.nrt + p->rb - 1) / p->rb);
+  if (!p->lds && !pick_kernel(p->mblocks, p->rb)) p->rb = 4;
+  const int64_t rows_per_group = p->lds ? (int64_t)WG_WAVES * p->rb : p->rb;
+  p->grid_x = (int)((L.nrt + rows_per_group - 1) / rows_per_group);
   {
     const int ks = std::min(force_ks, nkt);
     const int per = (nkt + ks - 1) / ks;
     p->ktiles_per_split = per;
     p->ksplit = p->grid_y = (nkt + per - 1) / per;
   }
-  p->lds_bytes = (size_t)WG_WAVES * p->rb * p->mblocks * 64 * sizeof(f32x4) + 16;
+  p->lds_bytes = p->lds ? lds_variant_bytes(p->mblocks, p->rb)
+                       : (size_t)WG_WAVES * p->rb * p->mblocks * 64 * sizeof(f32x4) + 16;
   return NVFP4V_OK;
 }
 
@@ -163,7 +208,7 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
   Plan p;
   int rc = make_plan(ctx, L, m, &p);
   if (rc) return rc;
-  if (epi.mode == EPI_PAIR && (p.rb & 1)) {  // (gate, up) row-tile pairs need an even R
+  if (!p.lds && epi.mode == EPI_PAIR && (p.rb & 1)) {  // (gate, up) row-tile pairs need an even R
     p.rb = 2;
     p.grid_x = (int)((L.nrt + p.rb - 1) / p.rb);
     p.lds_bytes = (size_t)WG_WAVES * p.rb * p.mblocks * 64 * sizeof(f32x4) + 16;
@@ -172,7 +217,7 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
     const size_t need = (size_t)p.ksplit * (size_t)m * (size_t)(L.nrt * ROWS_PER_TILE);
     if (need > ctx->partial_floats || (size_t)p.grid_x > ctx->n_counters) return NVFP4V_E_WORKSPACE;
   }
-  GemmKernel kern = pick_kernel(p.mblocks, p.rb);
+  GemmKernel kern = p.lds ? pick_lds_kernel(p.mblocks, p.rb) : pick_kernel(p.mblocks, p.rb);
   if (!kern) return NVFP4V_E_INVALID_ARG;
   if (fault_injected()) return NVFP4V_E_FAULT;
   GemmArgs g;
@@ -254,7 +299,8 @@ extern "C" int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64
   Plan p;
   int rc = make_plan(ctx, L, m, &p);
   if (rc) return rc;
-  snprintf(buf, len, "mfma16x16x32 mblocks=%d r=%d waves=%d grid=%dx%d ksplit=%d kt/split=%d lds=%zu",
-           p.mblocks, p.rb, p.waves, p.grid_x, p.grid_y, p.ksplit, p.ktiles_per_split, p.lds_bytes);
+  snprintf(buf, len, "mfma16x16x32 %s mblocks=%d r=%d waves=%d grid=%dx%d ksplit=%d kt/split=%d lds=%zu",
+           p.lds ? "act-in-lds/waves-split-n" : "waves-split-k", p.mblocks, p.rb, p.waves, p.grid_x,
+           p.grid_y, p.ksplit, p.ktiles_per_split, p.lds_bytes);
   return NVFP4V_OK;
 }

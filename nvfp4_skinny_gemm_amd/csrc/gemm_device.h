@@ -18,6 +18,14 @@ constexpr int WG_THREADS = 64 * WG_WAVES;
 constexpr int OOB = 0x7FFFFFF0;  // a buffer offset past every range: the load returns zeros
 constexpr int RAW_BUFFER_FLAGS = 0x00020000;
 
+// Work-group barrier that orders LDS only: waits for this wave's LDS
+// operations but not for its global loads in flight (a fence before the
+// barrier would wait for every outstanding load and empty the prefetch rings).
+__device__ inline void lds_barrier_wg() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left open
+  asm volatile("s_barrier" ::: "memory");
+}
+
 template <int SEL>
 __device__ inline uint32_t dq_pair(uint32_t codes, float s) {
   // Two E2M1 codes of byte SEL (low nibble = even k) -> fp32, times the block
@@ -201,6 +209,71 @@ struct GemmArgs {
   Epilogue epi;
 };
 
+// End of a work unit whose RT row tiles' sums sit in LDS: red[((w * RT + r) *
+// MB + mb) * 64 + lane] for slices w < NW (summed in slice order). With one
+// k-split the epilogue runs here; otherwise the unit publishes its partial tile
+// sums (system-coherent stores), takes a ticket, and the last of the row
+// block's splits to arrive sums them in split order 0..ksplit-1 and runs the
+// epilogue. The ticket slot follows the NW * RT * MB * 64 sums in LDS. Every
+// thread of the work-group calls this; it returns with the LDS free.
+template <int MB, int RT, int NW>
+__device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, f32x4 *red, int tid) {
+  const int M = g.M, N = g.N, nrt = g.nrt, ksplit = g.ksplit;
+  float *__restrict__ part = g.part;
+  unsigned *__restrict__ counters = g.counters;
+  const int rt0 = rb * RT;
+  const int npad = nrt * ROWS_PER_TILE;
+  constexpr int ITEMS = RT * MB * 64;
+  int nw = NW;
+  if (ksplit > 1) {
+    for (int it = tid; it < ITEMS; it += WG_THREADS) {
+      const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+      f32x4 v = red[((0 * RT + r) * MB + mb) * 64 + l];
+#pragma unroll
+      for (int wv = 1; wv < NW; ++wv) v += red[((wv * RT + r) * MB + mb) * 64 + l];
+      const int m = mb * 16 + (l & 15), rt = rt0 + r;
+      if (m >= M || rt >= nrt) continue;
+      float *dst = part + ((size_t)ks * M + m) * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(dst + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    // The partial stores have reached memory once this wave's counters drain.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    unsigned *s_ticket = reinterpret_cast<unsigned *>(red + NW * RT * MB * 64);
+    if (tid == 0)
+      *s_ticket = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __syncthreads();
+    const bool last = *s_ticket == (unsigned)(ksplit - 1);
+    __syncthreads();  // everyone has read the ticket before the slot is reused
+    if (!last) return;
+    // Last to arrive: sum the splits in order 0..ksplit-1 into slice 0.
+    for (int it = tid; it < ITEMS; it += WG_THREADS) {
+      const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+      const int m = mb * 16 + (l & 15), rt = rt0 + r;
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (m < M && rt < nrt) {
+        const float *src = part + (size_t)m * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int s2 = 1; s2 < ksplit; ++s2) {
+          const float *s2p = src + (size_t)s2 * M * npad;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] += __hip_atomic_load(s2p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+      }
+      red[((0 * RT + r) * MB + mb) * 64 + l] = v;
+    }
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    nw = 1;
+  }
+  epilogue<MB, RT>(red, nw, tid, M, N, nrt, rt0, g.ts, g.C, g.epi);
+  __syncthreads();  // LDS free for the next unit
+}
+
 // One work unit: row block `rb` (R row tiles) x k-split `ks`, by the whole
 // work-group. ABUF = 2 double-buffers the activation fragments; with ABUF = 1
 // the next k-tile's fragments are loaded after the last use of the current
@@ -211,12 +284,9 @@ struct GemmArgs {
 template <int MB, int R, int ABUF>
 __device__ inline void gemm_unit(const GemmArgs &g, int rb, int ks, f32x4 *red) {
   const uint8_t *__restrict__ act = g.act;
-  const int M = g.M, act_bytes = g.act_bytes, N = g.N, nrt = g.nrt, nkt = g.nkt;
+  const int M = g.M, act_bytes = g.act_bytes, nrt = g.nrt, nkt = g.nkt;
   const uint8_t *__restrict__ W = g.W;
-  const int kts_per_split = g.kts_per_split, ksplit = g.ksplit;
-  const float ts = g.ts;
-  float *__restrict__ part = g.part;
-  unsigned *__restrict__ counters = g.counters;
+  const int kts_per_split = g.kts_per_split;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int rt0 = rb * R;
@@ -306,57 +376,7 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int ks, f32x4 *red) 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
   __syncthreads();
-
-  const int npad = nrt * ROWS_PER_TILE;
-  constexpr int ITEMS = R * MB * 64;
-  int nw = WG_WAVES;
-  if (ksplit > 1) {
-    for (int it = tid; it < ITEMS; it += WG_THREADS) {
-      const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
-      f32x4 v = red[((0 * R + r) * MB + mb) * 64 + l];
-#pragma unroll
-      for (int wv = 1; wv < WG_WAVES; ++wv) v += red[((wv * R + r) * MB + mb) * 64 + l];
-      const int m = mb * 16 + (l & 15), rt = rt0 + r;
-      if (m >= M || rt >= nrt) continue;
-      float *dst = part + ((size_t)ks * M + m) * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __hip_atomic_store(dst + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    // The partial stores have reached memory once this wave's counters drain.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    unsigned *s_ticket = reinterpret_cast<unsigned *>(red + WG_WAVES * R * MB * 64);
-    if (tid == 0)
-      *s_ticket = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __syncthreads();
-    const bool last = *s_ticket == (unsigned)(ksplit - 1);
-    __syncthreads();  // everyone has read the ticket before the slot is reused
-    if (!last) return;
-    // Last to arrive: sum the splits in order 0..ksplit-1 into slot 0.
-    for (int it = tid; it < ITEMS; it += WG_THREADS) {
-      const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
-      const int m = mb * 16 + (l & 15), rt = rt0 + r;
-      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (m < M && rt < nrt) {
-        const float *src = part + (size_t)m * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        for (int s2 = 1; s2 < ksplit; ++s2) {
-          const float *s2p = src + (size_t)s2 * M * npad;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            v[i] += __hip_atomic_load(s2p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
-      }
-      red[((0 * R + r) * MB + mb) * 64 + l] = v;
-    }
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    nw = 1;
-  }
-  epilogue<MB, R>(red, nw, tid, M, N, nrt, rt0, ts, g.C, g.epi);
-  __syncthreads();  // LDS free for the next unit
+  unit_tail<MB, R, WG_WAVES>(g, rb, ks, red, tid);
 }
 
 
@@ -364,6 +384,122 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int ks, f32x4 *red) 
 template <int MB, int R>
 constexpr size_t unit_lds_bytes() {
   return (size_t)WG_WAVES * R * MB * 64 * sizeof(f32x4) + 16;
+}
+
+// The same GEMM with the activations staged in LDS once per work-group:
+// the 4 waves split N (wave w owns row tiles rt0 + w R .. + R - 1, RT = 4 R
+// per unit) and walk the same k-tiles in lockstep. Per k-tile i every thread
+// loads MB x 32 bytes of the packed activations (the work-group's copy) two
+// k-tiles ahead into registers and writes them to a two-slot LDS ring one
+// k-tile ahead; each wave reads its MFMA fragments from LDS and reuses them
+// across its R weight tiles. Weights stream through each wave's two-deep
+// register ring as in gemm_unit. One work-group barrier per k-tile.
+// `lds` holds 2 slots of MB * 8 KiB, then the RT tiles' sums and the ticket.
+template <int MB, int R>
+__device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t *lds) {
+  constexpr int RT = WG_WAVES * R;
+  constexpr int SLOT = MB * 8 * ACT_FRAG_BYTES;  // one k-tile of packed activations
+  constexpr int PER_THREAD = SLOT / WG_THREADS / 16;  // 16-byte chunks per thread (2 MB)
+  const int M = g.M, nrt = g.nrt, nkt = g.nkt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt0 = rb * RT + wave * R;
+  const int kA = ks * g.kts_per_split;
+  const int n = min(nkt, kA + g.kts_per_split) - kA;  // k-tiles of the unit (>= 1)
+  const int stripe_bytes = nkt * TILE_BYTES;
+  __amdgpu_buffer_rsrc_t rs[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rt = rt0 + r;
+    const uint8_t *base = g.W + (size_t)min(rt, nrt - 1) * (size_t)stripe_bytes;
+    rs[r] = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, rt < nrt ? stripe_bytes : 0,
+                                              RAW_BUFFER_FLAGS);
+  }
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.act, (short)0, g.act_bytes, RAW_BUFFER_FLAGS);
+  f32x4 *red = reinterpret_cast<f32x4 *>(lds + 2 * SLOT);
+
+  // Staging: k-tile j's packed block is contiguous (SLOT bytes at j * SLOT);
+  // thread t moves chunks t, t + 256, ... of it.
+  auto stage_load = [&](uint4 (&v)[PER_THREAD], int j) {
+    const int base = j < n ? (kA + j) * SLOT : OOB;
+#pragma unroll
+    for (int c = 0; c < PER_THREAD; ++c) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(ra, base + (c * WG_THREADS + tid) * 16, 0, 0);
+      __builtin_memcpy(&v[c], &x, 16);
+    }
+  };
+  auto stage_store = [&](const uint4 (&v)[PER_THREAD], int slot) {
+    uint4 *dst = reinterpret_cast<uint4 *>(lds + slot * SLOT);
+#pragma unroll
+    for (int c = 0; c < PER_THREAD; ++c) dst[c * WG_THREADS + tid] = v[c];
+  };
+  auto frags = [&](bf16x8 (&b)[MB][8], int slot) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(lds + slot * SLOT);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 x = src[(mb * 8 + q) * 64 + lane];
+        __builtin_memcpy(&b[mb][q], &x, 16);
+      }
+  };
+  // Rows >= M read zeros from the packed block (the packer wrote zeros there).
+
+  f32x4 acc[R][MB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[r][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  WTile w0[R], w1[R];
+  uint4 s0[PER_THREAD], s1[PER_THREAD];
+  stage_load(s0, 0);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_wtile(w0[r], rs[r], kA, true, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_load(s1, 1);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_wtile(w1[r], rs[r], kA + 1, n > 1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store(s0, 0);
+  stage_load(s0, 2);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Iteration i: barrier (slot i%2 holds k-tile i; slot (i+1)%2 is free),
+  // fragments of k-tile i, compute, stage k-tile i+1 into LDS, then request
+  // k-tile i+3's activations and k-tile i+2's weights.
+#define NVFP4V_LDS_STEP(W, S_NEXT, SLOT_I)                                               \
+  {                                                                                               \
+    lds_barrier_wg();                                                                             \
+    bf16x8 b[MB][8];                                                                              \
+    frags(b, SLOT_I);                                                                             \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) compute_wtile<MB>(W[r], b, acc[r]);            \
+    stage_store(S_NEXT, 1 - SLOT_I);                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    stage_load(S_NEXT, i + 3);                                                                    \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) load_wtile(W[r], rs[r], kA + i + 2, i + 2 < n, lane); \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+  }
+  int i = 0;
+  for (; i + 1 < n; i += 2) {
+    NVFP4V_LDS_STEP(w0, s1, 0)
+    ++i;
+    NVFP4V_LDS_STEP(w1, s0, 1)
+    --i;
+  }
+  if (i < n) NVFP4V_LDS_STEP(w0, s1, 0)
+#undef NVFP4V_LDS_STEP
+
+  // Each wave's tiles into slice 0 of the sums (tile wave * R + r), then the
+  // shared tail (split-K exchange, epilogue).
+  lds_barrier_wg();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
+  __syncthreads();
+  unit_tail<MB, RT, 1>(g, rb, ks, red, tid);
 }
 
 }  // namespace dev

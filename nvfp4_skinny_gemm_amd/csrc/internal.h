@@ -166,8 +166,10 @@ __host__ __device__ inline uint32_t quantize_block(const float *w, uint8_t *code
 // ---------------------------------------------------------------------------
 struct Plan {
   int mblocks;           // ceil(M / 16): 16-column MFMA blocks of activations
-  int rb;                // row tiles per work-group (every wave of it covers all of them)
-  int waves;             // waves per work-group; they split the group's k-range
+  int lds;               // 0: waves split the k-range, each loads its own activation
+                         //    fragments; 1: waves split N, activations staged in LDS
+  int rb;                // row tiles per wave item (variant 0: per work-group; 1: per wave)
+  int waves;             // waves per work-group
   int ksplit;            // work-groups along K (fixed-order reduction when > 1)
   int ktiles_per_split;  // k-tiles per work-group
   int grid_x, grid_y;    // row blocks, k splits

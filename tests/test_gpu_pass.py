@@ -135,6 +135,25 @@ def test_pass_equals_composition(torch_cuda, mode_ctx, m):
     assert torch.equal(outs[0].view(m, 3 * H), qkv)
 
 
+@pytest.mark.parametrize("plan", ["n:r=1,ks=2", "n:r=2,ks=1"])
+@pytest.mark.parametrize("m", [8, 24])
+def test_chain_pass_with_lds_plans(torch_cuda, ctx, monkeypatch, plan, m):
+    """The chained pass on the activations-in-LDS GEMM variant (fused scale and
+    gate/up pair epilogues included) equals the composition of single calls."""
+    torch = torch_cuda
+    H, I, L = 512, 1024, 2
+    monkeypatch.setenv("NVFP4V_PLAN", plan)
+    packed, arr = small_stack(torch, ctx, L, H, I, seed=5)
+    h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=3).view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
+    h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    trace = torch.empty((L, m, H), dtype=torch.bfloat16, device="cuda")
+    ctx.verify_pass(arr, H, I, h0[:m], ws, h_out, trace=trace)
+    ref = manual_chain(torch, ctx, packed, h0[:m], H, I)
+    for l in range(L):
+        assert torch.equal(trace[l].view(torch.int16), ref[l].view(torch.int16)), "layer %d" % l
+
+
 @pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
 def test_pass_longer_than_one_launch(torch_cuda, mode_ctx):
     """40 layers: the persistent kernel runs 32 layers per launch, so the chain
