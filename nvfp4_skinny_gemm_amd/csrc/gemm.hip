@@ -46,11 +46,11 @@ namespace {
 
 using namespace nvfp4v::dev;
 
-template <int MB, int R, int ABUF>
-__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MB, R>())))
+template <int MB, int R, int D>
+__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MB, R, D>())))
 void k_gemm(GemmArgs g) {
   extern __shared__ __align__(16) f32x4 red[];
-  gemm_unit<MB, R, ABUF>(g, blockIdx.x, blockIdx.y, red);
+  gemm_unit<MB, R, D>(g, blockIdx.x, blockIdx.y, red);
 }
 
 template <int MB, int R>
@@ -83,24 +83,36 @@ size_t lds_variant_bytes(int mb, int r) {
   return (size_t)2 * mb * 8 * ACT_FRAG_BYTES + (size_t)WG_WAVES * r * mb * 64 * sizeof(f32x4) + 16;
 }
 
-GemmKernel pick_kernel(int mb, int r) {
-  switch (mb * 16 + r) {
-    case 1 * 16 + 1: return k_gemm<1, 1, 2>;
-    case 1 * 16 + 2: return k_gemm<1, 2, 2>;
-    case 1 * 16 + 4: return k_gemm<1, 4, 2>;
-    case 1 * 16 + 8: return k_gemm<1, 8, 1>;
-    case 2 * 16 + 1: return k_gemm<2, 1, 2>;
-    case 2 * 16 + 2: return k_gemm<2, 2, 2>;
-    case 2 * 16 + 4: return k_gemm<2, 4, 1>;
-    case 2 * 16 + 8: return k_gemm<2, 8, 1>;
-    case 3 * 16 + 1: return k_gemm<3, 1, 1>;
-    case 3 * 16 + 2: return k_gemm<3, 2, 1>;
-    case 3 * 16 + 4: return k_gemm<3, 4, 1>;
-    case 4 * 16 + 1: return k_gemm<4, 1, 1>;
-    case 4 * 16 + 2: return k_gemm<4, 2, 1>;
-    case 4 * 16 + 4: return k_gemm<4, 4, 1>;
+// Ring depth per (row blocks, R): 2 by default, 1 where two copies of the
+// fragments do not fit, 3-4 for the short units of the 5120-row projections.
+GemmKernel pick_kernel(int mb, int r, int d) {
+  switch ((mb * 16 + r) * 8 + d) {
+    case (1 * 16 + 1) * 8 + 2: return k_gemm<1, 1, 2>;
+    case (1 * 16 + 2) * 8 + 2: return k_gemm<1, 2, 2>;
+    case (1 * 16 + 2) * 8 + 3: return k_gemm<1, 2, 3>;
+    case (1 * 16 + 2) * 8 + 4: return k_gemm<1, 2, 4>;
+    case (1 * 16 + 4) * 8 + 2: return k_gemm<1, 4, 2>;
+    case (1 * 16 + 4) * 8 + 3: return k_gemm<1, 4, 3>;
+    case (1 * 16 + 8) * 8 + 1: return k_gemm<1, 8, 1>;
+    case (2 * 16 + 1) * 8 + 2: return k_gemm<2, 1, 2>;
+    case (2 * 16 + 2) * 8 + 2: return k_gemm<2, 2, 2>;
+    case (2 * 16 + 4) * 8 + 1: return k_gemm<2, 4, 1>;
+    case (2 * 16 + 8) * 8 + 1: return k_gemm<2, 8, 1>;
+    case (3 * 16 + 1) * 8 + 1: return k_gemm<3, 1, 1>;
+    case (3 * 16 + 2) * 8 + 1: return k_gemm<3, 2, 1>;
+    case (3 * 16 + 4) * 8 + 1: return k_gemm<3, 4, 1>;
+    case (4 * 16 + 1) * 8 + 1: return k_gemm<4, 1, 1>;
+    case (4 * 16 + 2) * 8 + 1: return k_gemm<4, 2, 1>;
+    case (4 * 16 + 4) * 8 + 1: return k_gemm<4, 4, 1>;
     default: return nullptr;
   }
+}
+
+// The deepest ring compiled for (row blocks, R), capped at `want`.
+int ring_depth(int mb, int r, int want) {
+  for (int d = want; d >= 1; --d)
+    if (pick_kernel(mb, r, d)) return d;
+  return 0;
 }
 
 // Row-major A -> packed activations: one thread per 16-byte chunk.
@@ -153,6 +165,7 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
     p->rb = nrt >= 640 ? 4 : 2;
   int want_ks = (nkt >= 48 && nrt <= 640) ? 3 : 1;
   p->lds = 0;
+  int want_d = 2;
   // Activations staged in LDS (waves split N) where the N tile is wide enough
   // to give every CU work without a k-split: the LM head up to 32 rows, and the
   // 2.5k-9k-row projections at 17..32 rows, where the register-only variant's
@@ -169,14 +182,17 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
       p->rb = r;
       want_ks = k2 > 0 ? k2 : 1;
     } else if (std::sscanf(ov, "r=%d,ks=%d", &r, &k2) == 2 && (r == 1 || r == 2 || r == 4 || r == 8)) {
+      int d2 = 0;
       p->lds = 0;
       p->rb = r;
       want_ks = k2 > 0 ? k2 : 1;
+      if (std::sscanf(ov, "r=%*d,ks=%*d,d=%d", &d2) == 1 && d2 >= 1) want_d = d2;
     }
   }
   (void)ctx;
   int force_ks = want_ks;
-  if (!p->lds && !pick_kernel(p->mblocks, p->rb)) p->rb = 4;
+  if (!p->lds && !ring_depth(p->mblocks, p->rb, 4)) p->rb = 4;
+  p->depth = p->lds ? 0 : ring_depth(p->mblocks, p->rb, want_d);
   const int64_t rows_per_group = p->lds ? (int64_t)WG_WAVES * p->rb : p->rb;
   p->grid_x = (int)((L.nrt + rows_per_group - 1) / rows_per_group);
   {
@@ -210,6 +226,7 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
   if (rc) return rc;
   if (!p.lds && epi.mode == EPI_PAIR && (p.rb & 1)) {  // (gate, up) row-tile pairs need an even R
     p.rb = 2;
+    p.depth = ring_depth(p.mblocks, 2, p.depth);
     p.grid_x = (int)((L.nrt + p.rb - 1) / p.rb);
     p.lds_bytes = (size_t)WG_WAVES * p.rb * p.mblocks * 64 * sizeof(f32x4) + 16;
   }
@@ -217,7 +234,7 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
     const size_t need = (size_t)p.ksplit * (size_t)m * (size_t)(L.nrt * ROWS_PER_TILE);
     if (need > ctx->partial_floats || (size_t)p.grid_x > ctx->n_counters) return NVFP4V_E_WORKSPACE;
   }
-  GemmKernel kern = p.lds ? pick_lds_kernel(p.mblocks, p.rb) : pick_kernel(p.mblocks, p.rb);
+  GemmKernel kern = p.lds ? pick_lds_kernel(p.mblocks, p.rb) : pick_kernel(p.mblocks, p.rb, p.depth);
   if (!kern) return NVFP4V_E_INVALID_ARG;
   if (fault_injected()) return NVFP4V_E_FAULT;
   GemmArgs g;
@@ -299,8 +316,8 @@ extern "C" int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64
   Plan p;
   int rc = make_plan(ctx, L, m, &p);
   if (rc) return rc;
-  snprintf(buf, len, "mfma16x16x32 %s mblocks=%d r=%d waves=%d grid=%dx%d ksplit=%d kt/split=%d lds=%zu",
-           p.lds ? "act-in-lds/waves-split-n" : "waves-split-k", p.mblocks, p.rb, p.waves, p.grid_x,
-           p.grid_y, p.ksplit, p.ktiles_per_split, p.lds_bytes);
+  snprintf(buf, len, "mfma16x16x32 %s mblocks=%d r=%d depth=%d waves=%d grid=%dx%d ksplit=%d kt/split=%d lds=%zu",
+           p.lds ? "act-in-lds/waves-split-n" : "waves-split-k", p.mblocks, p.rb, p.depth, p.waves,
+           p.grid_x, p.grid_y, p.ksplit, p.ktiles_per_split, p.lds_bytes);
   return NVFP4V_OK;
 }

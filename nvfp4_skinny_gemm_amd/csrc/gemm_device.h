@@ -105,10 +105,12 @@ __device__ inline void compute_wtile(const WTile &t, const bf16x8 (&b)[MB][8], f
   }
 }
 
-// Occupancy target (waves per SIMD) for the register allocator.
-template <int MB, int R>
+// Occupancy target (waves per SIMD) for the register allocator: three when
+// the ring (D k-tiles of R weight tiles and MB fragment blocks), the
+// accumulators and ~40 working registers fit in 168 VGPRs, else two.
+template <int MB, int R, int D>
 constexpr int waves_per_simd() {
-  return (MB == 1 && R <= 2) ? 3 : 2;
+  return (D * (R * 9 + MB * 32) + R * MB * 4 + 40) <= 168 ? 3 : 2;
 }
 
 __device__ inline uint16_t bf16_bits(float x) {
@@ -275,13 +277,14 @@ __device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, f32x4 *red, 
 }
 
 // One work unit: row block `rb` (R row tiles) x k-split `ks`, by the whole
-// work-group. ABUF = 2 double-buffers the activation fragments; with ABUF = 1
-// the next k-tile's fragments are loaded after the last use of the current
-// ones (large M, where two copies do not fit in registers). `red` is the
-// work-group's LDS buffer of WG_WAVES * R * MB * 64 f32x4. Every thread of the
-// work-group calls this with the same arguments; it returns with the LDS
-// buffer free for the next unit.
-template <int MB, int R, int ABUF>
+// work-group; its 4 waves split the unit's k-tiles. D is the depth of each
+// wave's ring of k-tiles in flight (D = 1 at large M, where two copies of the
+// activation fragments do not fit in registers; 3 or 4 for short units, where
+// latency, not throughput, bounds the unit). `red` is the work-group's LDS
+// buffer of WG_WAVES * R * MB * 64 f32x4. Every thread of the work-group calls
+// this with the same arguments; it returns with the LDS buffer free for the
+// next unit.
+template <int MB, int R, int D>
 __device__ inline void gemm_unit(const GemmArgs &g, int rb, int ks, f32x4 *red) {
   const uint8_t *__restrict__ act = g.act;
   const int M = g.M, act_bytes = g.act_bytes, nrt = g.nrt, nkt = g.nkt;
@@ -316,56 +319,41 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int ks, f32x4 *red) 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[r][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  WTile w[R];
-  bf16x8 a0[MB][8];
-  load_afrag<MB>(a0, ra, kbeg, n > 0, M, lane);
+  // A ring of D k-tiles (weights and activation fragments) per wave: slot d
+  // holds k-tiles kbeg + d, kbeg + d + D, ...; each slot is refilled D
+  // k-tiles ahead right after it is consumed. The loop body consumes all D
+  // slots and issues the same loads in the same order every time (loads past
+  // the wave's range use an offset that returns zeros), with scheduling
+  // barriers keeping each refill in place, so the compiler's wait counts leave
+  // D - 1 k-tiles in flight. The remaining k-tiles (fewer than D) are
+  // computed after the loop without new loads.
+  WTile w[D][R];
+  bf16x8 a[D][MB][8];
 #pragma unroll
-  for (int r = 0; r < R; ++r) load_wtile(w[r], rs[r], kbeg, n > 0, lane);
-  if constexpr (ABUF == 2) {
-    // Two k-tiles of weights and activations in flight: ring w / a0 holds the
-    // even k-tiles of the wave's range, w1 / a1 the odd ones; each register
-    // set is refilled two k-tiles ahead as soon as it has been consumed.
-    WTile w1[R];
-    bf16x8 a1[MB][8];
-    __builtin_amdgcn_sched_barrier(0);  // set 0 is issued before set 1
+  for (int d = 0; d < D; ++d) {
+    load_afrag<MB>(a[d], ra, kbeg + d, d < n, M, lane);
 #pragma unroll
-    for (int r = 0; r < R; ++r) load_wtile(w1[r], rs[r], kbeg + 1, n > 1, lane);
-    load_afrag<MB>(a1, ra, kbeg + 1, n > 1, M, lane);
+    for (int r = 0; r < R; ++r) load_wtile(w[d][r], rs[r], kbeg + d, d < n, lane);
     __builtin_amdgcn_sched_barrier(0);
-    // The loop body always runs both halves, so the wait counts at its head
-    // see the same order of outstanding loads on every path; an odd k-tile
-    // left over is finished after it.
-    int i = 0;
-    for (; i + 1 < n; i += 2) {
+  }
+  int i = 0;
+  for (; i + D <= n; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        compute_wtile<MB>(w[r], a0, acc[r]);
-        load_wtile(w[r], rs[r], kbeg + i + 2, i + 2 < n, lane);
+        compute_wtile<MB>(w[d][r], a[d], acc[r]);
+        load_wtile(w[d][r], rs[r], kbeg + i + d + D, i + d + D < n, lane);
       }
-      load_afrag<MB>(a0, ra, kbeg + i + 2, i + 2 < n, M, lane);
-      // Keep each refill where it is: if the scheduler groups both sets'
-      // loads, the next compute waits for all of them (vmcnt 0).
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        compute_wtile<MB>(w1[r], a1, acc[r]);
-        load_wtile(w1[r], rs[r], kbeg + i + 3, i + 3 < n, lane);
-      }
-      load_afrag<MB>(a1, ra, kbeg + i + 3, i + 3 < n, M, lane);
+      load_afrag<MB>(a[d], ra, kbeg + i + d + D, i + d + D < n, M, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (i < n) {
+  }
 #pragma unroll
-      for (int r = 0; r < R; ++r) compute_wtile<MB>(w[r], a0, acc[r]);
-    }
-  } else {
-    for (int i = 0; i < n; ++i) {
+  for (int d = 0; d < D - 1; ++d) {
+    if (i + d < n) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        compute_wtile<MB>(w[r], a0, acc[r]);
-        load_wtile(w[r], rs[r], kbeg + i + 1, i + 1 < n, lane);
-      }
-      load_afrag<MB>(a0, ra, kbeg + i + 1, i + 1 < n, M, lane);
+      for (int r = 0; r < R; ++r) compute_wtile<MB>(w[d][r], a[d], acc[r]);
     }
   }
 

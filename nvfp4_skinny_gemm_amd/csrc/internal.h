@@ -170,6 +170,7 @@ struct Plan {
                          //    fragments; 1: waves split N, activations staged in LDS
   int rb;                // row tiles per wave item (variant 0: per work-group; 1: per wave)
   int waves;             // waves per work-group
+  int depth;             // variant 0: k-tiles in flight per wave (its register ring)
   int ksplit;            // work-groups along K (fixed-order reduction when > 1)
   int ktiles_per_split;  // k-tiles per work-group
   int grid_x, grid_y;    // row blocks, k splits

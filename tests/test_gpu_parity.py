@@ -255,11 +255,13 @@ def test_prepacked_activations_match(torch_cuda, ctx):
 
 
 @pytest.mark.parametrize("plan", ["r=1,ks=1", "r=2,ks=3", "r=4,ks=2", "r=8,ks=1", "r=8,ks=4", "r=1,ks=9",
+                                  "r=2,ks=1,d=4", "r=4,ks=2,d=3", "r=2,ks=5,d=3",
                                   "n:r=1,ks=1", "n:r=2,ks=1", "n:r=1,ks=3", "n:r=2,ks=5", "n:r=1,ks=18"])
 def test_plan_variants(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
     """Every tile-table variant the dispatcher can pick agrees with the oracle
-    ("n:" = activations staged in LDS, waves splitting N; a split of 18 leaves
-    one k-tile per work-group)."""
+    ("d=" = k-tiles in flight per wave, with ranges that are not a multiple of
+    it; "n:" = activations staged in LDS, waves splitting N; a split of 18
+    leaves one k-tile per work-group)."""
     torch = torch_cuda
     n, k = 272, 4608   # 17 row tiles (ragged for R = 2, 4, 8), 18 k-tiles
     g = np.random.default_rng(31)
