@@ -216,7 +216,9 @@ size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter, int
  *   NVFP4V_PASS_PERSISTENT  one cooperatively launched persistent kernel per
  *                           32 layers whose work-groups meet at a grid barrier
  *                           between dependent GEMMs.
- * Both compute the same values bit for bit. Errors: INVALID_ARG. */
+ * Each mode is deterministic (equal inputs give equal bits on every call); the
+ * two split K differently, so their fp32 sums can differ in the last bits.
+ * Errors: INVALID_ARG. */
 #define NVFP4V_PASS_CHAIN 0
 #define NVFP4V_PASS_PERSISTENT 1
 int nvfp4v_set_pass_mode(nvfp4v_ctx *ctx, int mode);
@@ -232,7 +234,9 @@ int nvfp4v_get_pass_mode(const nvfp4v_ctx *ctx);
  * h0 is bf16 [M][H]; the last layer's h goes to h_out (bf16 [M][H]). If trace
  * is not NULL, layer l's output h is also copied to trace[l][M][H]. Every
  * glue map is linear, so activations keep an O(1) RMS over the stack. Each
- * glue step runs in the epilogue of the GEMM that produces its input. In
+ * glue step runs in the epilogue of the GEMM that produces its input; fp32
+ * outputs are written for the last layer only (earlier ones would be
+ * overwritten unread). In
  * persistent mode a barrier wait that exceeds 2 s (it cannot while the launch
  * is co-resident) ends the kernel early and sets an error flag that
  * nvfp4v_pass_status reports; the outputs are then undefined. After the call returns, the

@@ -50,7 +50,8 @@ template <int MB, int R, int D>
 __global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MB, R, D>())))
 void k_gemm(GemmArgs g) {
   extern __shared__ __align__(16) f32x4 red[];
-  gemm_unit<MB, R, D>(g, blockIdx.x, blockIdx.y, red);
+  const int ks = blockIdx.y, kA = ks * g.kts_per_split;
+  gemm_unit<MB, R, D>(g, blockIdx.x, kA, min(g.nkt, kA + g.kts_per_split), ks, g.ksplit, red);
 }
 
 template <int MB, int R>

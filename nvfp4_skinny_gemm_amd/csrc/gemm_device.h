@@ -212,15 +212,17 @@ struct GemmArgs {
 };
 
 // End of a work unit whose RT row tiles' sums sit in LDS: red[((w * RT + r) *
-// MB + mb) * 64 + lane] for slices w < NW (summed in slice order). With one
-// k-split the epilogue runs here; otherwise the unit publishes its partial tile
-// sums (system-coherent stores), takes a ticket, and the last of the row
-// block's splits to arrive sums them in split order 0..ksplit-1 and runs the
-// epilogue. The ticket slot follows the NW * RT * MB * 64 sums in LDS. Every
-// thread of the work-group calls this; it returns with the LDS free.
+// MB + mb) * 64 + lane] for slices w < NW (summed in slice order). The unit is
+// piece `ks` of the `ksplit` pieces (consecutive k-ranges, in k order) its row
+// block is cut into. With one piece the epilogue runs here; otherwise the unit
+// publishes its partial tile sums (system-coherent stores), takes a ticket,
+// and the last of the row block's pieces to arrive sums them in piece order
+// 0..ksplit-1 and runs the epilogue. The ticket slot follows the NW * RT * MB
+// * 64 sums in LDS. Every thread of the work-group calls this; it returns with
+// the LDS free.
 template <int MB, int RT, int NW>
-__device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, f32x4 *red, int tid) {
-  const int M = g.M, N = g.N, nrt = g.nrt, ksplit = g.ksplit;
+__device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, int ksplit, f32x4 *red, int tid) {
+  const int M = g.M, N = g.N, nrt = g.nrt;
   float *__restrict__ part = g.part;
   unsigned *__restrict__ counters = g.counters;
   const int rt0 = rb * RT;
@@ -276,8 +278,9 @@ __device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, f32x4 *red, 
   __syncthreads();  // LDS free for the next unit
 }
 
-// One work unit: row block `rb` (R row tiles) x k-split `ks`, by the whole
-// work-group; its 4 waves split the unit's k-tiles. D is the depth of each
+// One work unit: row block `rb` (R row tiles) x k-tiles [kA, kB), piece `ks`
+// of the row block's `ksplit` pieces, by the whole work-group; its 4 waves
+// split the unit's k-tiles. D is the depth of each
 // wave's ring of k-tiles in flight (D = 1 at large M, where two copies of the
 // activation fragments do not fit in registers; 3 or 4 for short units, where
 // latency, not throughput, bounds the unit). `red` is the work-group's LDS
@@ -285,16 +288,13 @@ __device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, f32x4 *red, 
 // this with the same arguments; it returns with the LDS buffer free for the
 // next unit.
 template <int MB, int R, int D>
-__device__ inline void gemm_unit(const GemmArgs &g, int rb, int ks, f32x4 *red) {
+__device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int ks, int ksplit, f32x4 *red) {
   const uint8_t *__restrict__ act = g.act;
   const int M = g.M, act_bytes = g.act_bytes, nrt = g.nrt, nkt = g.nkt;
   const uint8_t *__restrict__ W = g.W;
-  const int kts_per_split = g.kts_per_split;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int rt0 = rb * R;
-  const int kA = ks * kts_per_split;
-  const int kB = min(nkt, kA + kts_per_split);
   const int len = kB - kA;
   const int kbeg = kA + (len * wave) / WG_WAVES;
   const int n = kA + (len * (wave + 1)) / WG_WAVES - kbeg;  // k-tiles of this wave
@@ -364,7 +364,7 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int ks, f32x4 *red) 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
   __syncthreads();
-  unit_tail<MB, R, WG_WAVES>(g, rb, ks, red, tid);
+  unit_tail<MB, R, WG_WAVES>(g, rb, ks, ksplit, red, tid);
 }
 
 
@@ -487,7 +487,7 @@ __device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
   __syncthreads();
-  unit_tail<MB, RT, 1>(g, rb, ks, red, tid);
+  unit_tail<MB, RT, 1>(g, rb, ks, g.ksplit, red, tid);
 }
 
 }  // namespace dev

@@ -89,7 +89,7 @@ unsigned glue_grid(int64_t total) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------------------
-// Workspace: the fp32 outputs of one layer (reused by every layer), then one
+// Workspace: the fp32 outputs of one layer (the last layer's are kept), then one
 // block of packed activations per layer and phase (each phase reads a buffer
 // of its own), then the packed h of the layer after the last one.
 // ---------------------------------------------------------------------------
@@ -341,7 +341,7 @@ __device__ inline GemmArgs phase_gemm(const PassArgs &a, int p) {
   g.counters = a.counters;
   Epilogue &e = g.epi;
   e.c = a.cst[j];
-  e.write_c = 1;
+  e.write_c = gl == a.last_layer ? 1 : 0;  // only the last layer's fp32 outputs are kept
   if (j == 0) {
     e.mode = EPI_SCALE, e.col0 = 2 * a.H, e.col1 = 3 * a.H, e.act = blk + a.act_off[1];
   } else if (j == 1) {
@@ -610,7 +610,8 @@ PhaseShape split_phase(int64_t n, int64_t nrt, int64_t nkt, int G, int R) {
 
 // The pass as four stream-ordered GEMM launches per layer. Each epilogue
 // writes the next GEMM's packed activations into the same per-layer blocks
-// the persistent kernel uses, so both modes produce identical bits.
+// the persistent kernel uses (the two schedules split K differently, so their
+// fp32 sums can differ in the last bits).
 int chain_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_t H, int64_t I,
                const uint16_t *h0, int64_t m, const PassWs &w, uint16_t *h_out, uint16_t *trace,
                hipStream_t stream) {
@@ -632,6 +633,8 @@ int chain_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_
     e_h.mode = EPI_SCALE, e_h.col0 = 0, e_h.col1 = (int)H, e_h.c = ci, e_h.act = a_next;
     e_h.rm0 = (l == n_layers - 1) ? h_out : nullptr;
     e_h.rm1 = trace ? trace + (size_t)l * m * H : nullptr;
+    // Only the last layer's fp32 outputs are kept: earlier ones would be overwritten unread.
+    e_o.write_c = e_g.write_c = e_d.write_c = e_h.write_c = (l == n_layers - 1) ? 1 : 0;
     rc = launch_gemm(ctx, a_h, m, H, (const uint8_t *)L.qkv, 3 * H, L.ts_qkv, w.C[0], stream, e_o);
     if (!rc) rc = launch_gemm(ctx, a_o, m, H, (const uint8_t *)L.o, H, L.ts_o, w.C[1], stream, e_g);
     if (!rc) rc = launch_gemm(ctx, a_g, m, H, (const uint8_t *)L.gate_up, 2 * I, L.ts_gate_up, w.C[2], stream, e_d);
