@@ -215,12 +215,18 @@ size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter, int
  *                           stream-ordered;
  *   NVFP4V_PASS_PERSISTENT  one cooperatively launched persistent kernel per
  *                           32 layers whose work-groups meet at a grid barrier
- *                           between dependent GEMMs.
+ *                           between dependent GEMMs;
+ *   NVFP4V_PASS_FLOW        one cooperatively launched persistent kernel per
+ *                           32 layers in which a producer wave per work-group
+ *                           streams weights into LDS across GEMM boundaries
+ *                           while its consumer waves compute (M <= 32; larger
+ *                           M runs the chained launches).
  * Each mode is deterministic (equal inputs give equal bits on every call); the
- * two split K differently, so their fp32 sums can differ in the last bits.
+ * modes split K differently, so their fp32 sums can differ in the last bits.
  * Errors: INVALID_ARG. */
 #define NVFP4V_PASS_CHAIN 0
 #define NVFP4V_PASS_PERSISTENT 1
+#define NVFP4V_PASS_FLOW 2
 int nvfp4v_set_pass_mode(nvfp4v_ctx *ctx, int mode);
 int nvfp4v_get_pass_mode(const nvfp4v_ctx *ctx);
 
@@ -237,7 +243,7 @@ int nvfp4v_get_pass_mode(const nvfp4v_ctx *ctx);
  * glue step runs in the epilogue of the GEMM that produces its input; fp32
  * outputs are written for the last layer only (earlier ones would be
  * overwritten unread). In
- * persistent mode a barrier wait that exceeds 2 s (it cannot while the launch
+ * the persistent and flow modes a barrier wait that exceeds 2 s (it cannot while the launch
  * is co-resident) ends the kernel early and sets an error flag that
  * nvfp4v_pass_status reports; the outputs are then undefined. After the call returns, the
  * workspace holds the last layer's fp32 GEMM outputs (qkv [M][3H] at offset 0,

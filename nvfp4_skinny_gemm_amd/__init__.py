@@ -28,6 +28,7 @@ E_WORKSPACE = -8
 E_TIMEOUT = -9
 PASS_CHAIN = 0
 PASS_PERSISTENT = 1
+PASS_FLOW = 2
 MAX_M = 64
 
 _lib = None
@@ -281,7 +282,7 @@ class Context:
         return int(load().nvfp4v_pass_status(self._h))
 
     def set_pass_mode(self, mode: int) -> None:
-        """PASS_CHAIN (four GEMM launches per layer) or PASS_PERSISTENT."""
+        """PASS_CHAIN (four GEMM launches per layer), PASS_PERSISTENT or PASS_FLOW."""
         _check(load().nvfp4v_set_pass_mode(self._h, int(mode)), "set_pass_mode")
 
     def get_pass_mode(self) -> int:

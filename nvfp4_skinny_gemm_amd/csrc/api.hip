@@ -81,7 +81,8 @@ extern "C" void nvfp4v_destroy(nvfp4v_ctx *ctx) {
 extern "C" int nvfp4v_last_hip_error(const nvfp4v_ctx *ctx) { return ctx ? ctx->last_hip : 0; }
 
 extern "C" int nvfp4v_set_pass_mode(nvfp4v_ctx *ctx, int mode) {
-  if (!ctx || (mode != NVFP4V_PASS_CHAIN && mode != NVFP4V_PASS_PERSISTENT)) return NVFP4V_E_INVALID_ARG;
+  if (!ctx || (mode != NVFP4V_PASS_CHAIN && mode != NVFP4V_PASS_PERSISTENT && mode != NVFP4V_PASS_FLOW))
+    return NVFP4V_E_INVALID_ARG;
   ctx->pass_mode = mode;
   return NVFP4V_OK;
 }

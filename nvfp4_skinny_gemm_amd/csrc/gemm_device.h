@@ -142,13 +142,59 @@ __device__ inline void store_next(const Epilogue &epi, int mblocks, int m, int j
   if (epi.rm1) *reinterpret_cast<uint2 *>(epi.rm1 + (size_t)m * cols + j) = v;
 }
 
+// One lane's final values of row tile rt and 16-row block mb (lane l holds
+// D[n = 16 rt + 4 (l / 16) + i][m = 16 mb + l % 16], i = 0..3): times ts,
+// into C and, for EPI_SCALE, into the next GEMM's activations. MB is the
+// number of 16-row blocks of the activations (the next GEMM's too).
+template <int MB>
+__device__ inline void epi_tile_lane(f32x4 v, int rt, int mb, int lane, int M, int N, int nrt, float ts,
+                                     float *C, const Epilogue &epi) {
+  const int m = mb * 16 + (lane & 15);
+  const int n0 = rt * ROWS_PER_TILE + 4 * (lane >> 4);
+  if (m >= M || rt >= nrt || n0 >= N) return;
+  v *= ts;
+  if (epi.write_c) {
+    float *dst = C + (size_t)m * N + n0;
+    if ((N & 3) == 0) {
+      *reinterpret_cast<f32x4 *>(dst) = v;
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (n0 + i < N) dst[i] = v[i];
+    }
+  }
+  if (epi.mode == EPI_SCALE && n0 >= epi.col0 && n0 < epi.col1) {
+    const float o[4] = {v[0] * epi.c, v[1] * epi.c, v[2] * epi.c, v[3] * epi.c};
+    store_next(epi, MB, m, n0 - epi.col0, epi.col1 - epi.col0, o);
+  }
+}
+
+// The same for a (gate, up) pair of row tiles rtg (even) and rtg + 1 (EPI_PAIR):
+// C in natural [gate | up] order and the glue sum into the next activations.
+template <int MB>
+__device__ inline void epi_pair_lane(f32x4 vg, f32x4 vu, int rtg, int mb, int lane, int M, int N, int nrt,
+                                     float ts, float *C, const Epilogue &epi) {
+  const int half = N / 2;
+  const int m = mb * 16 + (lane & 15);
+  if (m >= M || rtg + 1 >= nrt) return;
+  const int j0 = (rtg / 2) * ROWS_PER_TILE + 4 * (lane >> 4);
+  if (j0 >= half) return;
+  vg *= ts;
+  vu *= ts;
+  if (epi.write_c) {
+    *reinterpret_cast<f32x4 *>(C + (size_t)m * N + j0) = vg;
+    *reinterpret_cast<f32x4 *>(C + (size_t)m * N + half + j0) = vu;
+  }
+  const float o[4] = {glue_pair(vg[0], vu[0], epi.c), glue_pair(vg[1], vu[1], epi.c),
+                      glue_pair(vg[2], vu[2], epi.c), glue_pair(vg[3], vu[3], epi.c)};
+  store_next(epi, MB, m, j0, half, o);
+}
+
 // Final values of the work-group's tiles are red[w][r][mb][l] summed over the
 // first nw slots (wave order). Writes C (times ts) and the fused glue.
 template <int MB, int R>
 __device__ inline void epilogue(const f32x4 *red, int nw, int tid, int M, int N, int nrt, int rt0,
                                 float ts, float *C, const Epilogue &epi) {
   if (epi.mode == EPI_PAIR) {
-    const int half = N / 2;
     for (int it = tid; it < (R / 2) * MB * 64; it += WG_THREADS) {
       const int p = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
       f32x4 vg = red[((0 * R + 2 * p) * MB + mb) * 64 + l];
@@ -157,19 +203,7 @@ __device__ inline void epilogue(const f32x4 *red, int nw, int tid, int M, int N,
         vg += red[((wv * R + 2 * p) * MB + mb) * 64 + l];
         vu += red[((wv * R + 2 * p + 1) * MB + mb) * 64 + l];
       }
-      const int m = mb * 16 + (l & 15), rtg = rt0 + 2 * p;
-      if (m >= M || rtg + 1 >= nrt) continue;
-      const int j0 = (rtg / 2) * ROWS_PER_TILE + 4 * (l >> 4);
-      if (j0 >= half) continue;
-      vg *= ts;
-      vu *= ts;
-      if (epi.write_c) {
-        *reinterpret_cast<f32x4 *>(C + (size_t)m * N + j0) = vg;
-        *reinterpret_cast<f32x4 *>(C + (size_t)m * N + half + j0) = vu;
-      }
-      const float o[4] = {glue_pair(vg[0], vu[0], epi.c), glue_pair(vg[1], vu[1], epi.c),
-                          glue_pair(vg[2], vu[2], epi.c), glue_pair(vg[3], vu[3], epi.c)};
-      store_next(epi, MB, m, j0, half, o);
+      epi_pair_lane<MB>(vg, vu, rt0 + 2 * p, mb, l, M, N, nrt, ts, C, epi);
     }
     return;
   }
@@ -177,25 +211,7 @@ __device__ inline void epilogue(const f32x4 *red, int nw, int tid, int M, int N,
     const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
     f32x4 v = red[((0 * R + r) * MB + mb) * 64 + l];
     for (int wv = 1; wv < nw; ++wv) v += red[((wv * R + r) * MB + mb) * 64 + l];
-    // lane l of a tile holds D[n = 16 rt + 4 (l / 16) + i][m = 16 mb + l % 16]
-    const int m = mb * 16 + (l & 15);
-    const int rt = rt0 + r;
-    const int n0 = rt * ROWS_PER_TILE + 4 * (l >> 4);
-    if (m >= M || rt >= nrt || n0 >= N) continue;
-    v *= ts;
-    if (epi.write_c) {
-      float *dst = C + (size_t)m * N + n0;
-      if ((N & 3) == 0) {
-        *reinterpret_cast<f32x4 *>(dst) = v;
-      } else {
-        for (int i = 0; i < 4; ++i)
-          if (n0 + i < N) dst[i] = v[i];
-      }
-    }
-    if (epi.mode == EPI_SCALE && n0 >= epi.col0 && n0 < epi.col1) {
-      const float o[4] = {v[0] * epi.c, v[1] * epi.c, v[2] * epi.c, v[3] * epi.c};
-      store_next(epi, MB, m, n0 - epi.col0, epi.col1 - epi.col0, o);
-    }
+    epi_tile_lane<MB>(v, rt0 + r, mb, l, M, N, nrt, ts, C, epi);
   }
 }
 

@@ -96,6 +96,9 @@ def manual_chain(torch, ctx, packed, h0, H, I):
 
 
 MODES = [pytest.param(nv.PASS_CHAIN, id="chain"), pytest.param(nv.PASS_PERSISTENT, id="persistent")]
+# The flow schedule cuts K at other points than single calls do, so it is
+# checked against the oracle (and for determinism), not bitwise against them.
+ALL_MODES = MODES + [pytest.param(nv.PASS_FLOW, id="flow")]
 
 
 @pytest.fixture
@@ -173,7 +176,7 @@ def test_pass_longer_than_one_launch(torch_cuda, mode_ctx):
     assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16))
 
 
-@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
+@pytest.mark.parametrize("mode_ctx", ALL_MODES, indirect=True)
 def test_graph_replays_equal_eager(torch_cuda, mode_ctx):
     torch, ctx = torch_cuda, mode_ctx
     H, I, L, m = 512, 1024, 4, 16
@@ -240,7 +243,7 @@ def workspace_views(ws, m, H, I, L):
     return C, acts
 
 
-@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
+@pytest.mark.parametrize("mode_ctx", ALL_MODES, indirect=True)
 @pytest.mark.parametrize("m", [16, 24])
 def test_full_size_phases_against_oracle(torch_cuda, mode_ctx, oracle_mod, m):
     """Two full-size layers (H = 5120, I = 17408). For the last layer, every
@@ -249,9 +252,17 @@ def test_full_size_phases_against_oracle(torch_cuda, mode_ctx, oracle_mod, m):
     the workspace; every glue step (and the hand-over between layers) is
     checked bitwise against the oracle's glue on the fp32 outputs."""
     torch, ctx = torch_cuda, mode_ctx
-    H, I, L = 5120, 17408, 2
     log("full-size pass, mode %d, M = %d" % (ctx.get_pass_mode(), m))
-    packed, arr = small_stack(torch, ctx, L, H, I, seed=2)
+    run_and_check_last_layer(torch, ctx, oracle_mod, m, 5120, 17408, 2, seed=2, sample=384)
+
+
+def run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed, sample):
+    """Run the pass and check the last layer: every GEMM's fp32 output against
+    the oracle on `sample` weight rows (all rows if None), fed with the packed
+    activations the kernels read, taken back from the workspace; every glue
+    step and the hand-over between layers bitwise against the oracle's glue.
+    Returns the trace."""
+    packed, arr = small_stack(torch, ctx, L, H, I, seed=seed)
     a0 = synth.activations_bf16(64, H, seed=0, stream="pass/h0")
     h0 = torch.from_numpy(a0.view(np.int16)).cuda().view(torch.bfloat16)
     ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
@@ -260,11 +271,15 @@ def test_full_size_phases_against_oracle(torch_cuda, mode_ctx, oracle_mod, m):
     ctx.verify_pass(arr, H, I, h0[:m], ws, h_out, trace=trace)
     assert ctx.pass_status() == nv.OK
     torch.cuda.synchronize()
+    assert torch.isfinite(trace.float()).all(), "non-finite activations in the pass"
     C, acts = workspace_views(ws.cpu().numpy(), m, H, I, L)
+    for j in range(4):
+        assert np.isfinite(C[j]).all(), "non-finite fp32 output of GEMM %d" % j
     last = L - 1
     h_in = unpack_act(acts[last][0], m, H)
     assert np.array_equal(unpack_act(acts[0][0], m, H), a0[:m].view(np.uint16))
-    assert np.array_equal(h_in, trace[last - 1].view(torch.int16).cpu().numpy().view(np.uint16))
+    if L > 1:
+        assert np.array_equal(h_in, trace[last - 1].view(torch.int16).cpu().numpy().view(np.uint16))
     ins = [h_in, unpack_act(acts[last][1], m, H), unpack_act(acts[last][2], m, H),
            unpack_act(acts[last][3], m, I)]
     outs = [C[0].reshape(m, 3 * H), C[1].reshape(m, H), C[2].reshape(m, 2 * I), C[3].reshape(m, H)]
@@ -276,28 +291,92 @@ def test_full_size_phases_against_oracle(torch_cuda, mode_ctx, oracle_mod, m):
                                                       np.ascontiguousarray(outs[2][:, I:]), c_2))
     hq = h_out.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(hq, oracle_mod.glue_scale(outs[3], c_i))
-    # GEMMs: sampled rows of each projection against the oracle
+    # GEMMs: (sampled) rows of each projection against the oracle
     rng = np.random.default_rng(17)
     mats = [("qkv", ("q", "k", "v"), H, H), ("o", ("o",), H, H), ("gate_up", ("gate", "up"), I, H),
             ("down", ("down",), H, I)]
     for j, (name, parts, n_part, k) in enumerate(mats):
         n = n_part * len(parts)
-        rows = np.sort(rng.choice(n, 384, replace=False))
+        rows = np.arange(n) if sample is None else np.sort(rng.choice(n, sample, replace=False))
         w_rows = np.empty((len(rows), k), np.float32)
         for pi, part in enumerate(parts):
             sel = (rows // n_part) == pi
             if not sel.any():
                 continue
-            w = synth.weights_f32_cuda(n_part, k, seed=2, stream="t%d/%s" % (last, part))
+            w = synth.weights_f32_cuda(n_part, k, seed=seed, stream="t%d/%s" % (last, part))
             w_rows[sel] = w[torch.from_numpy(rows[sel] % n_part).cuda()].cpu().numpy()
             del w
         oc, osc = oracle_mod.quantize(w_rows)
         c_ref, s_ref = oracle_mod.gemm(ins[j], oc, osc)
         ok = oracle_mod.within_tolerance(outs[j][:, rows], c_ref, s_ref)
-        assert ok.all(), "%s: %d of %d sampled outputs outside 1e-5*S" % (name, (~ok).sum(), ok.size)
+        assert ok.all(), "%s: %d of %d checked outputs outside 1e-5*S" % (name, (~ok).sum(), ok.size)
+    return trace
+
+
+@pytest.mark.parametrize("shape", [(256, 512, 3), (2048, 8192, 2), (1040, 2064, 2)],
+                         ids=["tiny", "split-pieces", "ragged"])
+@pytest.mark.parametrize("m", [1, 8, 16, 17, 32])
+def test_flow_pass_against_oracle(torch_cuda, ctx, oracle_mod, shape, m):
+    """Flow schedule: the last layer's GEMMs (every row) against the oracle and
+    its glue bitwise. "tiny" leaves most work-groups without work, "split-pieces"
+    spreads row blocks over several work-groups (partial sums in k order),
+    "ragged" has row tiles and k-tiles that do not fill a row block or a
+    k-tile. The same pass again is bitwise identical."""
+    torch = torch_cuda
+    H, I, L = shape
+    ctx.set_pass_mode(nv.PASS_FLOW)
+    try:
+        log("flow pass H=%d I=%d L=%d M=%d" % (H, I, L, m))
+        t1 = run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed=4, sample=None)
+        t2 = run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed=4, sample=64)
+        assert torch.equal(t1.view(torch.int16), t2.view(torch.int16)), "flow pass not deterministic"
+    finally:
+        ctx.set_pass_mode(nv.PASS_CHAIN)
 
 
 @pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
+def test_ragged_k_pass_against_oracle(torch_cuda, mode_ctx, oracle_mod):
+    """H and I not multiples of the 256-wide k-tile: the padding of every
+    activation block is zeroed before the pass (stale workspace bytes would
+    otherwise meet the zero padding weights as 0 x NaN)."""
+    torch, ctx = torch_cuda, mode_ctx
+    for m in (1, 16):
+        run_and_check_last_layer(torch, ctx, oracle_mod, m, 1040, 2064, 2, seed=6, sample=None)
+
+
+@pytest.mark.parametrize("m", [16, 32])
+def test_flow_pass_longer_than_one_launch(torch_cuda, ctx, oracle_mod, m):
+    """40 layers: two flow launches (32 + 8 layers); the last layer is checked
+    against the oracle and the whole trace is deterministic."""
+    torch = torch_cuda
+    ctx.set_pass_mode(nv.PASS_FLOW)
+    try:
+        t1 = run_and_check_last_layer(torch, ctx, oracle_mod, m, 256, 512, 40, seed=9, sample=None)
+        t2 = run_and_check_last_layer(torch, ctx, oracle_mod, m, 256, 512, 40, seed=9, sample=None)
+        assert torch.equal(t1.view(torch.int16), t2.view(torch.int16))
+        assert torch.isfinite(t1.float()).all()
+    finally:
+        ctx.set_pass_mode(nv.PASS_CHAIN)
+
+
+def test_flow_pass_large_m_falls_back(torch_cuda, ctx):
+    """M > 32 in flow mode runs the chained launches: bitwise the composition."""
+    torch = torch_cuda
+    H, I, L, m = 256, 512, 2, 40
+    ctx.set_pass_mode(nv.PASS_FLOW)
+    try:
+        packed, arr = small_stack(torch, ctx, L, H, I)
+        h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=3).view(np.int16)).cuda().view(torch.bfloat16)
+        ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
+        h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+        ctx.verify_pass(arr, H, I, h0[:m], ws, h_out)
+        ref = manual_chain(torch, ctx, packed, h0[:m], H, I)
+        assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16))
+    finally:
+        ctx.set_pass_mode(nv.PASS_CHAIN)
+
+
+@pytest.mark.parametrize("mode_ctx", ALL_MODES, indirect=True)
 def test_full_stack_stays_finite_and_bounded(torch_cuda, mode_ctx):
     """64 layers at full size, M = 16: the linear glue keeps the RMS O(1)."""
     torch, ctx = torch_cuda, mode_ctx
