@@ -15,7 +15,11 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WG_WAVES = 4;
 constexpr int WG_THREADS = 64 * WG_WAVES;
-constexpr int OOB = 0x7FFFFFF0;  // a buffer offset past every range: the load returns zeros
+// A buffer offset past every range, so the load returns zeros. Every buffer
+// resource here covers at most 0x7FFF0000 bytes (the host checks), and the
+// largest constant or lane offset added to a base (< 32 KiB) keeps the sum
+// below INT_MAX, so the offset arithmetic never overflows.
+constexpr int OOB = 0x7FFF0000;
 constexpr int RAW_BUFFER_FLAGS = 0x00020000;
 
 // Work-group barrier that orders LDS only: waits for this wave's LDS
