@@ -194,11 +194,11 @@ __device__ __attribute__((always_inline)) inline void flow_produce(const PassArg
       const int rt = it.rb * RT + i;
       const uint32_t base = rt < f.nrt ? (uint32_t)(rt * f.nkt + it.kt) * TILE_BYTES : (uint32_t)OOB;
       uint8_t *t = dst + i * TILE_BYTES;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)t, 16, base + lane * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)t, 16, base + lane * 16, 0, 0, WEIGHT_AUX);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(t + CODE_HALF_BYTES), 16,
-                                               base + CODE_HALF_BYTES + lane * 16, 0, 0, 0);
+                                               base + CODE_HALF_BYTES + lane * 16, 0, 0, WEIGHT_AUX);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(t + SCALE_OFFSET), 4,
-                                               base + SCALE_OFFSET + lane * 4, 0, 0, 0);
+                                               base + SCALE_OFFSET + lane * 4, 0, 0, WEIGHT_AUX);
     }
     ++s;
     if (s > LAG) {

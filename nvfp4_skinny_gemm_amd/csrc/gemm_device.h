@@ -21,6 +21,11 @@ constexpr int WG_THREADS = 64 * WG_WAVES;
 // below INT_MAX, so the offset arithmetic never overflows.
 constexpr int OOB = 0x7FFF0000;
 constexpr int RAW_BUFFER_FLAGS = 0x00020000;
+// Cache policy of the weight loads: non-temporal. Each weight byte is read
+// once per pass, so its lines are marked to leave the caches first and the
+// packed activations, which every wave re-reads, stay resident (measured on
+// MI355X: 2 % faster over the pass at 16 rows, 3.5 % at one row).
+constexpr int WEIGHT_AUX = 2;
 
 // Work-group barrier that orders LDS only: waits for this wave's LDS
 // operations but not for its global loads in flight (a fence before the
@@ -66,9 +71,9 @@ struct WTile {
 // One row tile's k-tile (three loads per lane); `ok` false gives zeros.
 __device__ inline void load_wtile(WTile &t, __amdgpu_buffer_rsrc_t rs, int kt, bool ok, int lane) {
   const int base = ok ? kt * TILE_BYTES : OOB;
-  const auto c0 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + lane * 16, 0, 0);
-  const auto c1 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + CODE_HALF_BYTES + lane * 16, 0, 0);
-  const auto sc = __builtin_amdgcn_raw_buffer_load_b32(rs, base + SCALE_OFFSET + lane * 4, 0, 0);
+  const auto c0 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + lane * 16, 0, WEIGHT_AUX);
+  const auto c1 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + CODE_HALF_BYTES + lane * 16, 0, WEIGHT_AUX);
+  const auto sc = __builtin_amdgcn_raw_buffer_load_b32(rs, base + SCALE_OFFSET + lane * 4, 0, WEIGHT_AUX);
   __builtin_memcpy(&t.c[0], &c0, 16);
   __builtin_memcpy(&t.c[1], &c1, 16);
   t.s = (uint32_t)sc;

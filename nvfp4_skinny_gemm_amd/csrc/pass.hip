@@ -194,6 +194,8 @@ __device__ inline void load_item_w(WTile (&w)[R], const Item &it, const PassArgs
   for (int r = 0; r < R; ++r) {
     const int rt = it.rb * R + r;
     const int base = (real && rt < ps.nrt) ? rt * stripe + it.kt * TILE_BYTES : OOB;
+    // Default cache policy: with the non-temporal hint of the per-call GEMM
+    // this kernel measures 4 % slower (5.75 against 5.52 ms per pass).
     const auto c0 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + lane * 16, 0, 0);
     const auto c1 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + CODE_HALF_BYTES + lane * 16, 0, 0);
     const auto sc = __builtin_amdgcn_raw_buffer_load_b32(rs, base + SCALE_OFFSET + lane * 4, 0, 0);
