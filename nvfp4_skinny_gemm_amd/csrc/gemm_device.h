@@ -393,12 +393,6 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
 }
 
 
-// LDS bytes gemm_unit needs: the cross-wave reduction buffer plus the ticket.
-template <int MB, int R>
-constexpr size_t unit_lds_bytes() {
-  return (size_t)WG_WAVES * R * MB * 64 * sizeof(f32x4) + 16;
-}
-
 // The same GEMM with the activations staged in LDS once per work-group:
 // the 4 waves split N (wave w owns row tiles rt0 + w R .. + R - 1, RT = 4 R
 // per unit) and walk the same k-tiles in lockstep. Per k-tile i every thread
