@@ -65,6 +65,7 @@ extern "C" {
 #define NVFP4V_E_NONFINITE (-7)   /* quantiser input holds NaN or Inf          */
 #define NVFP4V_E_WORKSPACE (-8)   /* the request exceeds the context workspace */
 #define NVFP4V_E_TIMEOUT (-9)     /* a persistent pass gave up at a grid barrier */
+#define NVFP4V_E_DISPATCH (-10)   /* split-K pieces of a row block ran on two XCDs */
 
 #define NVFP4V_MAX_M 64
 
@@ -73,9 +74,24 @@ typedef struct nvfp4v_ctx nvfp4v_ctx;
 /* Create a context on HIP device `device` (>= 0). It holds the device's
  * properties, the tile table, and a split-K workspace (partial sums and
  * arrival counters) allocated here once, so that nvfp4v_verify_gemm never
- * allocates and can be captured in a HIP graph. The caller destroys it. */
+ * allocates and can be captured in a HIP graph. The caller destroys it.
+ * Create also runs a short synchronous dispatch probe: when the device deals
+ * the work-groups of a launch out to its XCDs round-robin by linear id (as
+ * gfx950 does in its one-partition mode), split-K GEMMs exchange their
+ * partial sums through the L2 of the one XCD that runs a row block's pieces;
+ * otherwise, or with NVFP4V_SPLITK_EXCHANGE=memory in the environment,
+ * through memory. Both give bitwise identical C. */
 int nvfp4v_create(nvfp4v_ctx **out, int device);
 void nvfp4v_destroy(nvfp4v_ctx *ctx);
+
+/* Synchronise the device, then report the device-side errors that GEMMs on
+ * this context recorded since it was created or last reported one:
+ * NVFP4V_E_DISPATCH if the pieces of some split-K row block ran on different
+ * XCDs, so that their exchange through one XCD's L2 could not meet (the C of
+ * that call is undefined; the context then clears the record and its arrival
+ * counters and exchanges through memory from then on), else NVFP4V_OK.
+ * Errors: INVALID_ARG, HIP. */
+int nvfp4v_device_status(nvfp4v_ctx *ctx);
 
 /* Human-readable text for a status code (static storage). */
 const char *nvfp4v_strerror(int status);

@@ -58,6 +58,7 @@ def load():
     lib.nvfp4v_strerror.argtypes = [c.c_int]
     lib.nvfp4v_strerror.restype = c.c_char_p
     lib.nvfp4v_last_hip_error.argtypes = [p]
+    lib.nvfp4v_device_status.argtypes = [p]
     lib.nvfp4v_quantize_host.argtypes = [p, i64, i64, p, p]
     lib.nvfp4v_quantize.argtypes = [p, p, i64, i64, p, p, p]
     lib.nvfp4v_encode_e4m3_host.argtypes = [p, i64, p]
@@ -171,6 +172,10 @@ class Context:
     @property
     def handle(self):
         return self._h
+
+    def device_status(self) -> int:
+        """Synchronise; NVFP4V_E_DISPATCH (-10) if a split-K GEMM saw an unexpected XCD, else 0."""
+        return int(load().nvfp4v_device_status(self._h))
 
     def last_hip_error(self) -> int:
         return int(load().nvfp4v_last_hip_error(self._h))

@@ -48,6 +48,8 @@ extern "C" int nvfp4v_create(nvfp4v_ctx **out, int device) {
   if (e == hipSuccess) e = hipMalloc((void **)&ctx->act, kActBytes);
   if (e == hipSuccess) e = hipMalloc((void **)&ctx->pass_sync, PASS_SYNC_WORDS * sizeof(unsigned));
   if (e == hipSuccess) e = hipMemset(ctx->pass_sync, 0, PASS_SYNC_WORDS * sizeof(unsigned));
+  if (e == hipSuccess) e = hipMalloc((void **)&ctx->dev_status, DEV_STATUS_BYTES);
+  if (e == hipSuccess) e = hipMemset(ctx->dev_status, 0, DEV_STATUS_BYTES);
   const char *tl = std::getenv("NVFP4V_PASS_TRACE");
   if (e == hipSuccess && tl && std::strcmp(tl, "1") == 0) {
     ctx->pass_timeline_words = 2 * PASS_TIMELINE_WGS * PASS_TIMELINE_PHASES;
@@ -64,6 +66,10 @@ extern "C" int nvfp4v_create(nvfp4v_ctx **out, int device) {
   ctx->partial_floats = kPartialFloats;
   ctx->n_counters = kCounters;
   ctx->act_bytes = kActBytes;
+  if (probe_dispatch(ctx) != NVFP4V_OK) {
+    nvfp4v_destroy(ctx);
+    return NVFP4V_E_HIP;
+  }
   *out = ctx;
   return NVFP4V_OK;
 }
@@ -75,7 +81,32 @@ extern "C" void nvfp4v_destroy(nvfp4v_ctx *ctx) {
   if (ctx->act) (void)hipFree(ctx->act);
   if (ctx->pass_sync) (void)hipFree(ctx->pass_sync);
   if (ctx->pass_timeline) (void)hipFree(ctx->pass_timeline);
+  if (ctx->dev_status) (void)hipFree(ctx->dev_status);
   delete ctx;
+}
+
+extern "C" int nvfp4v_device_status(nvfp4v_ctx *ctx) {
+  if (!ctx) return NVFP4V_E_INVALID_ARG;
+  hipError_t e = hipSetDevice(ctx->device);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  unsigned w[DEV_STATUS_BYTES / sizeof(unsigned)];
+  if (e == hipSuccess) e = hipMemcpy(w, ctx->dev_status, DEV_STATUS_BYTES, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_status(ctx, e);
+  unsigned begun = 0, done = 0;  // modulo 2^32 on both sides
+  for (int x = 0; x < 8; ++x) {
+    begun += w[x * DEV_LINE_WORDS + DEV_ROWS_BEGUN];
+    done += w[x * DEV_LINE_WORDS + DEV_ROWS_DONE];
+  }
+  if (begun == done) return NVFP4V_OK;
+  // Some row block's pieces ran on two XCDs, so their tickets went to two
+  // L2s and its C was never written. Clear the counts and the tickets, and
+  // exchange through memory from now on.
+  ctx->xcd_local = 0;
+  e = hipMemset(ctx->dev_status, 0, DEV_STATUS_BYTES);
+  if (e == hipSuccess) e = hipMemset(ctx->counters, 0, ctx->n_counters * sizeof(unsigned));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_status(ctx, e);
+  return NVFP4V_E_DISPATCH;
 }
 
 extern "C" int nvfp4v_last_hip_error(const nvfp4v_ctx *ctx) { return ctx ? ctx->last_hip : 0; }
@@ -115,6 +146,7 @@ extern "C" const char *nvfp4v_strerror(int status) {
     case NVFP4V_E_NONFINITE: return "non-finite input";
     case NVFP4V_E_WORKSPACE: return "request exceeds the context's split-K workspace";
     case NVFP4V_E_TIMEOUT: return "a persistent pass timed out at a grid barrier";
+    case NVFP4V_E_DISPATCH: return "the pieces of a split-K row block ran on different XCDs (outputs undefined)";
     default: return "unknown status";
   }
 }

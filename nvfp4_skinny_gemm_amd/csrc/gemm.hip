@@ -37,6 +37,8 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <vector>
 
 #include "gemm_device.h"
 
@@ -50,6 +52,8 @@ template <int MB, int R, int D>
 __global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MB, R, D>())))
 void k_gemm(GemmArgs g) {
   extern __shared__ __align__(16) f32x4 red[];
+  if ((int)blockIdx.x >= g.nrb) return;  // grid padding
+  if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
   const int ks = blockIdx.y, kA = ks * g.kts_per_split;
   gemm_unit<MB, R, D>(g, blockIdx.x, kA, min(g.nkt, kA + g.kts_per_split), ks, g.ksplit, red);
 }
@@ -63,6 +67,8 @@ template <int MB, int R>
 __global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(lds_waves_per_simd<MB, R>())))
 void k_gemm_lds(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
+  if ((int)blockIdx.x >= g.nrb) return;  // grid padding
+  if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
   gemm_unit_lds<MB, R>(g, blockIdx.x, blockIdx.y, lds);
 }
 
@@ -116,6 +122,12 @@ int ring_depth(int mb, int r, int want) {
   return 0;
 }
 
+// Dispatch probe: every work-group records the XCD it runs on.
+__global__ void k_xcd_probe(unsigned *out) {
+  if (threadIdx.x == 0)
+    out[blockIdx.x + blockIdx.y * gridDim.x] = (unsigned)__builtin_amdgcn_s_getreg(XCC_ID_HWREG) & 0xFu;
+}
+
 // Row-major A -> packed activations: one thread per 16-byte chunk.
 // `sync` (optional): the persistent pass's barrier words, zeroed here because
 // this kernel starts every pass (its grid always has more threads than words).
@@ -153,6 +165,12 @@ namespace nvfp4v {
 //    (the 151936-row head) want R = 4 at M <= 16 and R = 8 at M <= 32;
 //  * at M > 32, R = 4 except for the narrowest matrices (R = 2).
 // NVFP4V_PLAN="r=<R>,ks=<ksplit>" overrides both (used by tuning sweeps).
+static void finish_grid(const nvfp4v_ctx *ctx, Plan *p) {
+  p->nrb = p->grid_x;
+  p->xcd_local = p->ksplit > 1 && ctx && ctx->xcd_local;
+  if (p->xcd_local) p->grid_x = (p->grid_x + 7) & ~7;
+}
+
 int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
   p->mblocks = (int)((m + 15) / 16);
   p->waves = WG_WAVES;
@@ -190,7 +208,6 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
       if (std::sscanf(ov, "r=%*d,ks=%*d,d=%d", &d2) == 1 && d2 >= 1) want_d = d2;
     }
   }
-  (void)ctx;
   int force_ks = want_ks;
   if (!p->lds && !ring_depth(p->mblocks, p->rb, 4)) p->rb = 4;
   p->depth = p->lds ? 0 : ring_depth(p->mblocks, p->rb, want_d);
@@ -204,6 +221,39 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
   }
   p->lds_bytes = p->lds ? lds_variant_bytes(p->mblocks, p->rb)
                        : (size_t)WG_WAVES * p->rb * p->mblocks * 64 * sizeof(f32x4) + 16;
+  finish_grid(ctx, p);
+  return NVFP4V_OK;
+}
+
+// The split-K exchange through one XCD's L2 needs the work-groups whose
+// linear ids are congruent mod 8 to run on one XCD: gfx950 in its one-partition
+// mode deals the work-groups of a dispatch out to its XCDs round-robin by id
+// (the XCD that takes id 0 can differ between queues, which is harmless).
+// This launches grids of the shapes the GEMM uses and checks exactly that
+// property in each; if a launch breaks it (another partition mode or device),
+// the context keeps the exchange through memory. At run time the GEMM counts
+// the row blocks begun and completed, and nvfp4v_device_status reports a
+// difference. NVFP4V_SPLITK_EXCHANGE=memory forces the exchange through memory.
+int probe_dispatch(nvfp4v_ctx *ctx) {
+  ctx->xcd_local = 0;
+  const char *env = std::getenv("NVFP4V_SPLITK_EXCHANGE");
+  if (env && std::strcmp(env, "memory") == 0) return NVFP4V_OK;
+  static const int shapes[][2] = {{4096, 1}, {8, 512}, {240, 2}, {1088, 3}, {160, 3}, {16, 9}, {80, 6}};
+  unsigned *buf = reinterpret_cast<unsigned *>(ctx->partials);  // free before the first GEMM
+  std::vector<unsigned> h(4096);
+  bool ok = true;
+  for (const auto &sh : shapes) {
+    const int n = sh[0] * sh[1];
+    hipError_t e = hipMemset(buf, 0xFF, (size_t)n * sizeof(unsigned));
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_xcd_probe, dim3((unsigned)sh[0], (unsigned)sh[1]), dim3(64), 0, 0, buf);
+      e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipMemcpy(h.data(), buf, (size_t)n * sizeof(unsigned), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(ctx, e);
+    for (int i = 0; i < n && ok; ++i) ok = h[i] <= 15u && h[i] == h[i & 7];
+  }
+  ctx->xcd_local = ok ? 1 : 0;
   return NVFP4V_OK;
 }
 
@@ -230,10 +280,11 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
     p.depth = ring_depth(p.mblocks, 2, p.depth);
     p.grid_x = (int)((L.nrt + p.rb - 1) / p.rb);
     p.lds_bytes = (size_t)WG_WAVES * p.rb * p.mblocks * 64 * sizeof(f32x4) + 16;
+    finish_grid(ctx, &p);
   }
   if (p.ksplit > 1) {
     const size_t need = (size_t)p.ksplit * (size_t)m * (size_t)(L.nrt * ROWS_PER_TILE);
-    if (need > ctx->partial_floats || (size_t)p.grid_x > ctx->n_counters) return NVFP4V_E_WORKSPACE;
+    if (need > ctx->partial_floats || (size_t)p.nrb > ctx->n_counters) return NVFP4V_E_WORKSPACE;
   }
   GemmKernel kern = p.lds ? pick_lds_kernel(p.mblocks, p.rb) : pick_kernel(p.mblocks, p.rb, p.depth);
   if (!kern) return NVFP4V_E_INVALID_ARG;
@@ -253,6 +304,9 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
   g.part = ctx->partials;
   g.counters = ctx->counters;
   g.epi = epi;
+  g.nrb = p.nrb;
+  g.xcd_local = p.xcd_local;
+  g.status = ctx->dev_status;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.grid_x, (unsigned)p.grid_y), dim3(WG_THREADS),
                      p.lds_bytes, stream, g);
   return hip_status(ctx, hipGetLastError());
@@ -300,7 +354,7 @@ extern "C" int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m,
   if (rc) return rc;
   if (p.ksplit > 1) {
     const size_t need = (size_t)p.ksplit * (size_t)m * (size_t)(L.nrt * ROWS_PER_TILE);
-    if (need > ctx->partial_floats || (size_t)p.grid_x > ctx->n_counters) return NVFP4V_E_WORKSPACE;
+    if (need > ctx->partial_floats || (size_t)p.nrb > ctx->n_counters) return NVFP4V_E_WORKSPACE;
   }
   if (fault_injected()) return NVFP4V_E_FAULT;
   rc = launch_pack_act(ctx, a, m, k, ctx->act, stream);
@@ -317,8 +371,9 @@ extern "C" int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64
   Plan p;
   int rc = make_plan(ctx, L, m, &p);
   if (rc) return rc;
-  snprintf(buf, len, "mfma16x16x32 %s mblocks=%d r=%d depth=%d waves=%d grid=%dx%d ksplit=%d kt/split=%d lds=%zu",
+  snprintf(buf, len, "mfma16x16x32 %s mblocks=%d r=%d depth=%d waves=%d grid=%dx%d ksplit=%d kt/split=%d lds=%zu exchange=%s",
            p.lds ? "act-in-lds/waves-split-n" : "waves-split-k", p.mblocks, p.rb, p.depth, p.waves,
-           p.grid_x, p.grid_y, p.ksplit, p.ktiles_per_split, p.lds_bytes);
+           p.grid_x, p.grid_y, p.ksplit, p.ktiles_per_split, p.lds_bytes,
+           p.ksplit == 1 ? "none" : p.xcd_local ? "xcd-l2" : "memory");
   return NVFP4V_OK;
 }

@@ -26,6 +26,9 @@ constexpr int RAW_BUFFER_FLAGS = 0x00020000;
 // packed activations, which every wave re-reads, stay resident (measured on
 // MI355X: 2 % faster over the pass at 16 rows, 3.5 % at one row).
 constexpr int WEIGHT_AUX = 2;
+// s_getreg_b32 operand of HW_REG_XCC_ID (register 20, all 32 bits; bits 3:0
+// hold the XCD the wave runs on).
+constexpr int XCC_ID_HWREG = 0xF814;
 
 // Work-group barrier that orders LDS only: waits for this wave's LDS
 // operations but not for its global loads in flight (a fence before the
@@ -234,17 +237,43 @@ struct GemmArgs {
   float *C, *part;
   unsigned *counters;
   Epilogue epi;
+  // Row blocks of the launch. The grid's x may be padded past it (to a
+  // multiple of 8 for the exchange below); padding work-groups do nothing.
+  int nrb = 0x7FFFFFFF;
+  // Split-K exchange through the L2 of one XCD (unit_tail): set when the grid's
+  // x is a multiple of 8, so that the pieces of a row block have linear ids
+  // congruent mod 8, and the dispatch probe found such ids on one XCD. The
+  // row blocks begun and completed are then counted in `status` (below).
+  int xcd_local = 0;
+  unsigned *status = nullptr;
 };
+
+// Row-block counts of the exchange through one XCD's L2, in the context's
+// status lines: line x (DEV_LINE_WORDS words) counts, for work-groups on XCD
+// x, the row blocks begun (by their piece 0) and completed (by their last
+// arriver). A row block whose pieces ran on two XCDs took its tickets in two
+// L2s, so none of its pieces saw the last ticket: it is begun and never
+// completed, and the host reports the difference. Fire-and-forget atomics, off
+// the exchange's critical path.
+__device__ inline void count_row_block(unsigned *status, int which) {
+  const unsigned x = (unsigned)__builtin_amdgcn_s_getreg(XCC_ID_HWREG) & 7u;
+  __hip_atomic_fetch_add(status + x * DEV_LINE_WORDS + which, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 // End of a work unit whose RT row tiles' sums sit in LDS: red[((w * RT + r) *
 // MB + mb) * 64 + lane] for slices w < NW (summed in slice order). The unit is
 // piece `ks` of the `ksplit` pieces (consecutive k-ranges, in k order) its row
 // block is cut into. With one piece the epilogue runs here; otherwise the unit
-// publishes its partial tile sums (system-coherent stores), takes a ticket,
-// and the last of the row block's pieces to arrive sums them in piece order
-// 0..ksplit-1 and runs the epilogue. The ticket slot follows the NW * RT * MB
-// * 64 sums in LDS. Every thread of the work-group calls this; it returns with
-// the LDS free.
+// publishes its partial tile sums, takes a ticket, and the last of the row
+// block's pieces to arrive sums them in piece order 0..ksplit-1 and runs the
+// epilogue. The exchange meets either in memory (system-scope stores, ticket
+// and loads, which bypass the dies' L2s) or, with g.xcd_local, in the L2 of
+// the one XCD that runs all pieces of the row block: plain stores (the vector
+// L1 writes through to the L2), a ticket atomic executed in that L2, and loads
+// that read through to it. Each row block's partial lines are read once per
+// launch, by its last arriver, so no L1 can hold a stale copy of them. The
+// ticket slot follows the NW * RT * MB * 64 sums in LDS. Every thread of the
+// work-group calls this; it returns with the LDS free.
 template <int MB, int RT, int NW>
 __device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, int ksplit, f32x4 *red, int tid) {
   const int M = g.M, N = g.N, nrt = g.nrt;
@@ -255,6 +284,7 @@ __device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, int ksplit, 
   constexpr int ITEMS = RT * MB * 64;
   int nw = NW;
   if (ksplit > 1) {
+    const bool local = g.xcd_local != 0;
     for (int it = tid; it < ITEMS; it += WG_THREADS) {
       const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
       f32x4 v = red[((0 * RT + r) * MB + mb) * 64 + l];
@@ -263,40 +293,65 @@ __device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, int ksplit, 
       const int m = mb * 16 + (l & 15), rt = rt0 + r;
       if (m >= M || rt >= nrt) continue;
       float *dst = part + ((size_t)ks * M + m) * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
+      if (local) {
+        *reinterpret_cast<f32x4 *>(dst) = v;
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __hip_atomic_store(dst + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(dst + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
     }
-    // The partial stores have reached memory once this wave's counters drain.
-    __builtin_amdgcn_s_waitcnt(0);
+    // The partial stores are acknowledged (by the L2, or by memory) once this
+    // wave's counter drains; the clobber keeps the compiler from moving them
+    // below the wait.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     unsigned *s_ticket = reinterpret_cast<unsigned *>(red + NW * RT * MB * 64);
     if (tid == 0)
-      *s_ticket = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      *s_ticket = local ? __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                        : __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __syncthreads();
     const bool last = *s_ticket == (unsigned)(ksplit - 1);
     __syncthreads();  // everyone has read the ticket before the slot is reused
     if (!last) return;
+    if (local && tid == 0) count_row_block(g.status, DEV_ROWS_DONE);
     // Last to arrive: sum the splits in order 0..ksplit-1 into slice 0.
+    // (Buffer loads with sc0 read through the L1; every offset lies inside the
+    // ksplit * M * npad floats of the partials.)
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)part, (short)0, (int)((size_t)ksplit * M * npad * sizeof(float)), RAW_BUFFER_FLAGS);
     for (int it = tid; it < ITEMS; it += WG_THREADS) {
       const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
       const int m = mb * 16 + (l & 15), rt = rt0 + r;
       f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
       if (m < M && rt < nrt) {
-        const float *src = part + (size_t)m * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
+        const size_t off = (size_t)m * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
+        if (local) {
+          for (int s2 = 0; s2 < ksplit; ++s2) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rp, (int)((off + (size_t)s2 * M * npad) * sizeof(float)), 0, 1);
+            f32x4 y;
+            __builtin_memcpy(&y, &x, 16);
+            v = s2 == 0 ? y : v + y;
+          }
+        } else {
+          const float *src = part + off;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        for (int s2 = 1; s2 < ksplit; ++s2) {
-          const float *s2p = src + (size_t)s2 * M * npad;
+          for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          for (int s2 = 1; s2 < ksplit; ++s2) {
+            const float *s2p = src + (size_t)s2 * M * npad;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            v[i] += __hip_atomic_load(s2p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            for (int i = 0; i < 4; ++i)
+              v[i] += __hip_atomic_load(s2p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          }
         }
       }
       red[((0 * RT + r) * MB + mb) * 64 + l] = v;
     }
     __syncthreads();
-    if (tid == 0) __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (tid == 0) {
+      if (local) __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      else __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
     nw = 1;
   }
   epilogue<MB, RT>(red, nw, tid, M, N, nrt, rt0, g.ts, g.C, g.epi);
@@ -407,7 +462,7 @@ __device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
   constexpr int RT = WG_WAVES * R;
   constexpr int SLOT = MB * 8 * ACT_FRAG_BYTES;  // one k-tile of packed activations
   constexpr int PER_THREAD = SLOT / WG_THREADS / 16;  // 16-byte chunks per thread (2 MB)
-  const int M = g.M, nrt = g.nrt, nkt = g.nkt;
+  const int nrt = g.nrt, nkt = g.nkt;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rt0 = rb * RT + wave * R;

@@ -173,8 +173,10 @@ struct Plan {
   int depth;             // variant 0: k-tiles in flight per wave (its register ring)
   int ksplit;            // work-groups along K (fixed-order reduction when > 1)
   int ktiles_per_split;  // k-tiles per work-group
-  int grid_x, grid_y;    // row blocks, k splits
+  int grid_x, grid_y;    // row blocks (padded to a multiple of 8 with xcd_local), k splits
   size_t lds_bytes;      // cross-wave reduction buffer
+  int nrb;               // row blocks
+  int xcd_local;         // split-K exchange through one XCD's L2 (else through memory)
 };
 
 }  // namespace nvfp4v
@@ -196,7 +198,16 @@ struct nvfp4v_ctx {
                                       // real-time clock at phase start and at work done
   size_t pass_timeline_words = 0;
   int last_pass_phases = 0;
+  int xcd_local = 0;  // the dispatch probe allows the split-K exchange through one XCD's L2
+  unsigned *dev_status = nullptr;  // DEV_STATUS_BYTES: row-block counts of that exchange
 };
+
+// Context status lines: 8 lines of DEV_LINE_WORDS words, line x holding the
+// row blocks begun and completed on XCD x by split-K GEMMs that exchange
+// through one XCD's L2 (the two totals differ only if a row block's pieces
+// ran on two XCDs).
+constexpr int DEV_LINE_WORDS = 32, DEV_ROWS_BEGUN = 0, DEV_ROWS_DONE = 1;
+constexpr size_t DEV_STATUS_BYTES = 8 * DEV_LINE_WORDS * sizeof(unsigned);
 
 // Timeline capacity: 2 stamps for each of up to 1024 work-groups and 512 phases.
 constexpr size_t PASS_TIMELINE_WGS = 1024, PASS_TIMELINE_PHASES = 512;
@@ -206,6 +217,8 @@ int fault_injected();  // NVFP4V_FAULT=launch
 int hip_status(nvfp4v_ctx *ctx, hipError_t e);
 bool aligned16(const void *p);
 int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p);
+// Sets ctx->xcd_local from a dispatch probe (synchronous; at create).
+int probe_dispatch(nvfp4v_ctx *ctx);
 // Enqueue A (row-major bf16) -> packed activations (no argument checks).
 int launch_pack_act(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
                     hipStream_t stream, unsigned *sync = nullptr);

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_strerror(lib):
-    for code in range(0, -9, -1):
+    for code in range(0, -11, -1):
         assert nv.strerror(code) and nv.strerror(code) != "unknown status"
     assert nv.strerror(-99) == "unknown status"
 

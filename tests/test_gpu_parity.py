@@ -275,3 +275,58 @@ def test_plan_variants(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
         log("plan %s M=%d: %s" % (plan, m, ctx.describe_plan(n, k, m)))
         c = ctx.verify_gemm(a_dev[:m], packed, n, k, ts=1.25).cpu().numpy()
         assert_parity(oracle_mod, c, c_ref[:m], s_ref[:m], "plan %s M=%d" % (plan, m))
+
+
+def test_dispatch_probe_enables_xcd_exchange(torch_cuda, ctx):
+    """On MI355X (one partition, 8 XCDs dealt work-groups round-robin by id) the
+    probe at create turns on the split-K exchange through one XCD's L2; the
+    environment switch turns it off."""
+    assert "exchange=xcd-l2" in ctx.describe_plan(5120, 17408, 16)
+    assert "exchange=none" in ctx.describe_plan(15360, 5120, 16)
+    import os
+
+    os.environ["NVFP4V_SPLITK_EXCHANGE"] = "memory"
+    try:
+        c2 = nv.Context(0)
+    finally:
+        del os.environ["NVFP4V_SPLITK_EXCHANGE"]
+    try:
+        assert "exchange=memory" in c2.describe_plan(5120, 17408, 16)
+    finally:
+        c2.close()
+
+
+@pytest.mark.parametrize("plan", ["r=2,ks=3", "r=1,ks=9", "r=4,ks=2,d=3", "n:r=1,ks=3", "n:r=2,ks=5",
+                                  "n:r=1,ks=18"])
+def test_splitk_exchange_paths_agree(torch_cuda, ctx, monkeypatch, plan):
+    """The exchange through one XCD's L2 (grid padded to a multiple of 8, plain
+    partial stores, ticket in that L2) and the exchange through memory give
+    bitwise identical C, on a ragged matrix (17 row tiles) and on the full-size
+    down projection; no work-group reports an unexpected XCD."""
+    torch = torch_cuda
+    monkeypatch.setenv("NVFP4V_SPLITK_EXCHANGE", "memory")
+    ctx_mem = nv.Context(0)
+    monkeypatch.delenv("NVFP4V_SPLITK_EXCHANGE")
+    try:
+        g = np.random.default_rng(41)
+        monkeypatch.setenv("NVFP4V_PLAN", plan)
+        for (n, k, ms) in [(272, 4608, (1, 16, 33, 64)), (5120, 17408, (16,))]:
+            codes, scales = random_codes_scales(g, n, k)
+            packed = pack_dev(torch, ctx, codes, scales, n, k)
+            a_dev = bf16_dev(torch, synth.activations_bf16(64, k, seed=7, outliers=True))
+            for m in ms:
+                d_l2, d_mem = ctx.describe_plan(n, k, m), ctx_mem.describe_plan(n, k, m)
+                log("plan %s N=%d M=%d: %s | %s" % (plan, n, m, d_l2, d_mem))
+                if "ksplit=1 " in d_l2:  # the variant is not built for this M: no split
+                    assert "exchange=none" in d_l2 and "exchange=none" in d_mem
+                else:
+                    assert "exchange=xcd-l2" in d_l2 and "exchange=memory" in d_mem
+                c1 = ctx.verify_gemm(a_dev[:m], packed, n, k, ts=0.75)
+                c2 = ctx_mem.verify_gemm(a_dev[:m], packed, n, k, ts=0.75)
+                c3 = ctx.verify_gemm(a_dev[:m], packed, n, k, ts=0.75)
+                assert torch.equal(c1.view(torch.int32), c2.view(torch.int32)), (plan, n, m)
+                assert torch.equal(c1.view(torch.int32), c3.view(torch.int32)), (plan, n, m)
+        assert ctx.device_status() == 0
+        assert ctx_mem.device_status() == 0
+    finally:
+        ctx_mem.close()
