@@ -389,7 +389,7 @@ def main():
     traffic = traffic_from_profile(kernel_source_hash())
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": "k_gemm (verify GEMM) at M=%d over the pass's four projection shapes" % args.m,
+                "kernel": "verify GEMM (k_gemm / k_gemm_lds as the tile table picks) at M=%d over the pass's four projection shapes" % args.m,
                 "avg_launch_us": round(gms * 1e3 / launches, 2),
                 "algorithmic_bytes_per_launch": round(gbytes / launches), "launches": launches,
                 "per_shape": per_shape}

@@ -154,16 +154,24 @@ __global__ void k_pack_act(const uint16_t *__restrict__ A, int M, int K, int mbl
 
 namespace nvfp4v {
 
-// Tile table for gfx950, from a sweep of R (row tiles per work-group, sharing
-// one activation fragment) and ksplit (work-groups along K) over the layer
-// shapes [15360|5120|34816 x 5120], [5120 x 17408] and [151936 x 5120] at
-// M = 1, 16, 32, 64 (median of 9 timed launches over 1 GiB of rotated weight
-// copies each):
-//  * splitting K across work-groups only pays for K-heavy, narrow matrices
-//    (down: 3 splits); everywhere else one work-group covers all of K;
-//  * R = 2 is best up to about 4096 row tiles at M <= 32; very wide matrices
-//    (the 151936-row head) want R = 4 at M <= 16 and R = 8 at M <= 32;
-//  * at M > 32, R = 4 except for the narrowest matrices (R = 2).
+// Tile table for gfx950. R = row tiles per wave item sharing one activation
+// fragment, ksplit = work-groups along K, "LDS" = the variant whose waves
+// split N and share activations staged in LDS. From sweeps of R in {1,2,4,8}
+// x ksplit in {1,2,3,4,6,8} x both variants, one projection at a time, inside
+// the graph-replayed 64-layer pass (the other projections at their chosen
+// plans), at M = 1, 8, 9, 16, 17, 24, 32, and of single launches over 1 GiB
+// of rotated weight copies for the LM head and M > 32:
+//  * up to 8 rows: R = 2 everywhere, K split 3 for the K-heavy narrow down
+//    projection [5120 x 17408];
+//  * 9..16 rows (twice the activation bytes per k-tile): R = 4 for the
+//    ~1k-row-tile q|k|v, LDS with K split 3 for the 2k-row-tile gate|up, LDS
+//    with K split 6 for down, R = 2 for o;
+//  * 17..32 rows: R = 4 with K split 3 for down, R = 4 for q|k|v and gate|up,
+//    R = 2 for o;
+//  * the 151936-row LM head: LDS with R = 2 per wave up to 32 rows;
+//  * beyond 32 rows: R = 4 except for the narrowest matrices (R = 2).
+// Split-K exchanges meet in one XCD's L2 (unit_tail), which is what makes the
+// K splits at 9..16 rows pay.
 // NVFP4V_PLAN="r=<R>,ks=<ksplit>" overrides both (used by tuning sweeps).
 static void finish_grid(const nvfp4v_ctx *ctx, Plan *p) {
   p->nrb = p->grid_x;
@@ -176,24 +184,28 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
   p->waves = WG_WAVES;
   const int64_t nrt = L.nrt;
   const int nkt = (int)L.nkt;
-  if (p->mblocks == 1)
-    p->rb = nrt >= 4096 && m > 1 ? 4 : 2;
-  else if (p->mblocks == 2)
-    p->rb = nrt >= 4096 ? 8 : 2;
-  else
-    p->rb = nrt >= 640 ? 4 : 2;
-  int want_ks = (nkt >= 48 && nrt <= 640) ? 3 : 1;
+  const bool narrow = nrt <= 640, deep = nkt >= 48;  // o and down vs q|k|v and gate|up
+  int want_ks = 1;
   p->lds = 0;
   int want_d = 2;
-  // Activations staged in LDS (waves split N) where the N tile is wide enough
-  // to give every CU work without a k-split: the LM head up to 32 rows, and the
-  // 2.5k-9k-row projections at 17..32 rows, where the register-only variant's
-  // per-wave fragment reloads cost the most (measured on MI355X).
-  if (p->mblocks <= 2 && nrt >= 4096) {
-    p->lds = 1, p->rb = 2, want_ks = 1;
-  } else if (p->mblocks == 2 && nrt >= 640 && nkt < 48) {
-    p->lds = 1, p->rb = 1, want_ks = 1;
+  if (p->mblocks == 1) {
+    p->rb = nrt >= 4096 && m > 1 ? 4 : 2;
+    if (deep && narrow) {
+      want_ks = 3;
+      if (m > 8) p->lds = 1, p->rb = 1, want_ks = 6;
+    } else if (m > 8 && !narrow && nrt < 4096) {
+      if (nrt >= 2048) p->lds = 1, p->rb = 1, want_ks = 3;
+      else p->rb = 4;
+    }
+  } else if (p->mblocks == 2) {
+    p->rb = nrt >= 4096 ? 8 : narrow && !deep ? 2 : 4;
+    if (deep && narrow) want_ks = 3;
+  } else {
+    p->rb = nrt >= 640 ? 4 : 2;
+    if (deep && narrow) want_ks = 3;
   }
+  // The LM head up to 32 rows: activations staged in LDS, R = 2 per wave.
+  if (p->mblocks <= 2 && nrt >= 4096) p->lds = 1, p->rb = 2, want_ks = 1;
   if (const char *ov = std::getenv("NVFP4V_PLAN")) {
     int r = 0, k2 = 0;
     if (std::sscanf(ov, "n:r=%d,ks=%d", &r, &k2) == 2 && pick_lds_kernel(p->mblocks, r)) {
