@@ -205,6 +205,45 @@ def test_graph_replays_equal_eager(torch_cuda, mode_ctx):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("m", [8, 16, 24])
+def test_graph_replays_equal_eager_full_size(torch_cuda, ctx, m):
+    """Full-size layers in the chained schedule, whose tile table splits K at
+    these row counts (down at 8; gate|up and down at 16; down at 24) and
+    exchanges the partial sums through one XCD's L2: graph replays equal the
+    eager pass bitwise, with split eager GEMMs on the same context in between
+    (they share the arrival counters), and no row block reports pieces on two
+    XCDs."""
+    torch = torch_cuda
+    H, I, L = 5120, 17408, 2
+    packed, arr = small_stack(torch, ctx, L, H, I, seed=3)
+    h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=8).view(np.int16)).cuda().view(torch.bfloat16)
+    d_in = torch.from_numpy(synth.activations_bf16(64, I, seed=9).view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
+    eager = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    ctx.verify_pass(arr, H, I, h0[:m], ws, eager)
+    torch.cuda.synchronize()
+    d_ref = ctx.verify_gemm(d_in[:m], packed[1]["down"], H, I).clone()
+    log("M=%d down plan: %s" % (m, ctx.describe_plan(H, I, m)))
+    out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ctx.verify_pass(arr, H, I, h0[:m], ws, out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ctx.verify_pass(arr, H, I, h0[:m], ws, out)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), "replay %d" % rep
+        d = ctx.verify_gemm(d_in[:m], packed[1]["down"], H, I)
+        torch.cuda.synchronize()
+        assert torch.equal(d.view(torch.int32), d_ref.view(torch.int32)), "eager down after replay %d" % rep
+    assert ctx.device_status() == 0
+
+
 def align256(x):
     return (x + 255) // 256 * 256
 
