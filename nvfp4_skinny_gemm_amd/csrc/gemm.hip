@@ -169,7 +169,9 @@ namespace nvfp4v {
 //  * 17..32 rows: R = 4 with K split 3 for down, R = 4 for q|k|v and gate|up,
 //    R = 2 for o;
 //  * the 151936-row LM head: LDS with R = 2 per wave up to 32 rows;
-//  * beyond 32 rows: R = 4 except for the narrowest matrices (R = 2).
+//  * beyond 32 rows: R = 4 with K split 3 for down, and for the narrow
+//    square matrices beyond 48 rows; R = 2 for those up to 48 rows; R = 4
+//    for the wide ones.
 // Split-K exchanges meet in one XCD's L2 (unit_tail), which is what makes the
 // K splits at 9..16 rows pay.
 // NVFP4V_PLAN="r=<R>,ks=<ksplit>" overrides both (used by tuning sweeps).
@@ -201,8 +203,8 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
     p->rb = nrt >= 4096 ? 8 : narrow && !deep ? 2 : 4;
     if (deep && narrow) want_ks = 3;
   } else {
-    p->rb = nrt >= 640 ? 4 : 2;
-    if (deep && narrow) want_ks = 3;
+    p->rb = nrt >= 640 || deep || p->mblocks == 4 ? 4 : 2;
+    if (narrow && (deep || p->mblocks == 4)) want_ks = 3;
   }
   // The LM head up to 32 rows: activations staged in LDS, R = 2 per wave.
   if (p->mblocks <= 2 && nrt >= 4096) p->lds = 1, p->rb = 2, want_ks = 1;
