@@ -163,8 +163,9 @@ namespace nvfp4v {
 // of rotated weight copies for the LM head and M > 32:
 //  * up to 8 rows: R = 2 everywhere, K split 3 for the K-heavy narrow down
 //    projection [5120 x 17408];
-//  * 9..16 rows (twice the activation bytes per k-tile): R = 4 for the
-//    ~1k-row-tile q|k|v, LDS with K split 3 for the 2k-row-tile gate|up, LDS
+//  * 9..16 rows (twice the activation bytes per k-tile): R = 4 for q|k|v (960
+//    row tiles), LDS with K split 3 from 1024 row tiles (gate|up: 2176 in the
+//    pass, 1088 for one of the pair alone, 15 % faster than R = 4 there), LDS
 //    with K split 6 for down, R = 2 for o;
 //  * 17..32 rows: R = 4 with K split 3 for down, R = 4 for q|k|v and gate|up,
 //    R = 2 for o;
@@ -196,7 +197,7 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
       want_ks = 3;
       if (m > 8) p->lds = 1, p->rb = 1, want_ks = 6;
     } else if (m > 8 && !narrow && nrt < 4096) {
-      if (nrt >= 2048) p->lds = 1, p->rb = 1, want_ks = 3;
+      if (nrt >= 1024) p->lds = 1, p->rb = 1, want_ks = 3;
       else p->rb = 4;
     }
   } else if (p->mblocks == 2) {
