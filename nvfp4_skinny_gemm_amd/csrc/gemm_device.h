@@ -274,7 +274,7 @@ __device__ inline void count_row_block(unsigned *status, int which) {
 // launch, by its last arriver, so no L1 can hold a stale copy of them. The
 // ticket slot follows the NW * RT * MB * 64 sums in LDS. Every thread of the
 // work-group calls this; it returns with the LDS free.
-template <int MB, int RT, int NW>
+template <int MB, int RT, int NW, bool REDUCER = false>
 __device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, int ksplit, f32x4 *red, int tid) {
   const int M = g.M, N = g.N, nrt = g.nrt;
   float *__restrict__ part = g.part;
@@ -283,7 +283,75 @@ __device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, int ksplit, 
   const int npad = nrt * ROWS_PER_TILE;
   constexpr int ITEMS = RT * MB * 64;
   int nw = NW;
-  if (ksplit > 1) {
+  if (REDUCER && ksplit > 1 && g.xcd_local) {
+    // Designated reducer (exchange through one XCD's L2 only): the row
+    // block's last piece, which has the highest linear id and is dispatched
+    // after its siblings, keeps its own partial in LDS and waits for the
+    // others to publish theirs, instead of every piece publishing and the last
+    // to arrive reducing. The siblings never wait on anything, and they were
+    // dispatched before the reducer, so the wait ends; a 1 s bound on the
+    // 100 MHz clock makes any other outcome an unfinished row block, which the
+    // begun/completed counts report. Their tickets use the low 16 bits; the
+    // reducer polls with an atomic add in the high bits (an atomic executes in
+    // the L2; a plain load could keep hitting a stale L1 line) and then
+    // clears the word. The sum keeps the split order 0..ksplit-1.
+    unsigned *s_flag = reinterpret_cast<unsigned *>(red + NW * RT * MB * 64);
+    if (ks != ksplit - 1) {
+      for (int it = tid; it < ITEMS; it += WG_THREADS) {
+        const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+        f32x4 v = red[((0 * RT + r) * MB + mb) * 64 + l];
+#pragma unroll
+        for (int wv = 1; wv < NW; ++wv) v += red[((wv * RT + r) * MB + mb) * 64 + l];
+        const int m = mb * 16 + (l & 15), rt = rt0 + r;
+        if (m >= M || rt >= nrt) continue;
+        *reinterpret_cast<f32x4 *>(part + ((size_t)ks * M + m) * npad + rt * ROWS_PER_TILE + 4 * (l >> 4)) = v;
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) (void)__hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return;
+    }
+    if (tid == 0) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      unsigned n = 0;
+      while (((n = __hip_atomic_fetch_add(&counters[rb], 0x10000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) &
+              0xFFFFu) < (unsigned)(ksplit - 1)) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > 100000000ull) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      const bool ok = (n & 0xFFFFu) == (unsigned)(ksplit - 1);
+      *s_flag = ok ? 1u : 0u;
+      if (ok) {
+        __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        count_row_block(g.status, DEV_ROWS_DONE);
+      }
+    }
+    __syncthreads();
+    if (!*s_flag) return;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)part, (short)0, (int)((size_t)ksplit * M * npad * sizeof(float)), RAW_BUFFER_FLAGS);
+    for (int it = tid; it < ITEMS; it += WG_THREADS) {
+      const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
+      f32x4 own = red[((0 * RT + r) * MB + mb) * 64 + l];
+#pragma unroll
+      for (int wv = 1; wv < NW; ++wv) own += red[((wv * RT + r) * MB + mb) * 64 + l];
+      const int m = mb * 16 + (l & 15), rt = rt0 + r;
+      f32x4 v = own;
+      if (m < M && rt < nrt) {
+        const size_t off = (size_t)m * npad + rt * ROWS_PER_TILE + 4 * (l >> 4);
+        for (int s2 = 0; s2 < ksplit - 1; ++s2) {
+          const auto x = __builtin_amdgcn_raw_buffer_load_b128(rp, (int)((off + (size_t)s2 * M * npad) * sizeof(float)), 0, 1);
+          f32x4 y;
+          __builtin_memcpy(&y, &x, 16);
+          v = s2 == 0 ? y : v + y;
+        }
+        v += own;
+      }
+      red[((0 * RT + r) * MB + mb) * 64 + l] = v;
+    }
+    __syncthreads();
+    nw = 1;
+  } else if (ksplit > 1) {
     const bool local = g.xcd_local != 0;
     for (int it = tid; it < ITEMS; it += WG_THREADS) {
       const int r = it / (MB * 64), mb = (it / 64) % MB, l = it & 63;
@@ -561,7 +629,7 @@ __device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
   __syncthreads();
-  unit_tail<MB, RT, 1>(g, rb, ks, g.ksplit, red, tid);
+  unit_tail<MB, RT, 1, true>(g, rb, ks, g.ksplit, red, tid);
 }
 
 }  // namespace dev
