@@ -26,6 +26,7 @@ E_FAULT = -6
 E_NONFINITE = -7
 E_WORKSPACE = -8
 E_TIMEOUT = -9
+E_DISPATCH = -10
 PASS_CHAIN = 0
 PASS_PERSISTENT = 1
 PASS_FLOW = 2
@@ -174,7 +175,7 @@ class Context:
         return self._h
 
     def device_status(self) -> int:
-        """Synchronise; NVFP4V_E_DISPATCH (-10) if a split-K GEMM saw an unexpected XCD, else 0."""
+        """Synchronise; E_DISPATCH if some split-K row block's pieces ran on two XCDs, else 0."""
         return int(load().nvfp4v_device_status(self._h))
 
     def last_hip_error(self) -> int:

@@ -127,6 +127,8 @@ def test_other_argument_errors(lib):
     assert lib.nvfp4v_staircase(ctx, 16, 128, 1, 2, 0, 0, 0, us) == nv.E_INVALID_ARG
     buf = ctypes.create_string_buffer(8)
     assert lib.nvfp4v_describe_plan(ctx, 16, 128, 0, buf, 8) == nv.E_M_RANGE
+    assert lib.nvfp4v_device_status(None) == nv.E_INVALID_ARG
+    assert nv.strerror(nv.E_DISPATCH) != "unknown status"
 
 
 def test_host_quantiser_matches_oracle(oracle_mod):
