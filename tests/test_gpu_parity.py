@@ -180,12 +180,19 @@ def full_shape_case(torch, ctx, oracle_mod, n, k, ms, stream):
 
 
 def test_gate_up_projection_full(torch_cuda, ctx, oracle_mod):
-    full_shape_case(torch_cuda, ctx, oracle_mod, 17408, 5120, [1, 8, 16, 24, 32], "gate_up")
+    # every regime of the tile table: up to 8 rows, 9..16 (the LDS-staged K split
+    # from 1024 row tiles), 17..32, 33..48 and 49..64
+    full_shape_case(torch_cuda, ctx, oracle_mod, 17408, 5120, [1, 8, 9, 16, 24, 32, 33, 49, 64], "gate_up")
+
+
+def test_square_projection_full(torch_cuda, ctx, oracle_mod):
+    # the 5120 x 5120 projections, including the K split of 3 at 49..64 rows
+    full_shape_case(torch_cuda, ctx, oracle_mod, 5120, 5120, [1, 9, 16, 17, 33, 48, 49, 64], "o")
 
 
 def test_down_projection_full(torch_cuda, ctx, oracle_mod):
     torch = torch_cuda
-    packed, a_dev, outs = full_shape_case(torch, ctx, oracle_mod, 5120, 17408, [1, 8, 16, 24, 32],
+    packed, a_dev, outs = full_shape_case(torch, ctx, oracle_mod, 5120, 17408, [1, 8, 9, 16, 24, 32, 33, 64],
                                           "down")
     # determinism: the same call again is bitwise identical
     for m in (1, 16, 32):
