@@ -597,17 +597,21 @@ __device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
   __builtin_amdgcn_sched_barrier(0);
 
   // Iteration i: barrier (slot i%2 holds k-tile i; slot (i+1)%2 is free),
-  // fragments of k-tile i, compute, stage k-tile i+1 into LDS, then request
-  // k-tile i+3's activations and k-tile i+2's weights.
+  // fragments of k-tile i, stage k-tile i+1 into LDS and request k-tile i+3's
+  // activations (before the compute: 0.8 % faster over the pass at 12-16
+  // rows), compute, then request k-tile i+2's weights into the registers the
+  // compute has just freed.
 #define NVFP4V_LDS_STEP(W, S_NEXT, SLOT_I)                                               \
   {                                                                                               \
     lds_barrier_wg();                                                                             \
     bf16x8 b[MB][8];                                                                              \
     frags(b, SLOT_I);                                                                             \
-    _Pragma("unroll") for (int r = 0; r < R; ++r) compute_wtile<MB>(W[r], b, acc[r]);            \
     stage_store(S_NEXT, 1 - SLOT_I);                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                            \
     stage_load(S_NEXT, i + 3);                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) compute_wtile<MB>(W[r], b, acc[r]);            \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
     _Pragma("unroll") for (int r = 0; r < R; ++r) load_wtile(W[r], rs[r], kA + i + 2, i + 2 < n, lane); \
     __builtin_amdgcn_sched_barrier(0);                                                            \
   }
