@@ -91,7 +91,8 @@ size_t lds_variant_bytes(int mb, int r) {
 }
 
 // Ring depth per (row blocks, R): 2 by default, 1 where two copies of the
-// fragments do not fit, 3-4 for the short units of the 5120-row projections.
+// fragments do not fit. Depths 3-4 are reachable only through NVFP4V_PLAN
+// (measured slower in the pass at 1-16 rows, kept for the override's tests).
 GemmKernel pick_kernel(int mb, int r, int d) {
   switch ((mb * 16 + r) * 8 + d) {
     case (1 * 16 + 1) * 8 + 2: return k_gemm<1, 1, 2>;
