@@ -67,6 +67,10 @@ def _load():
     lib.oracle_gemm_cols.argtypes = [p, i64, i64, p, p, p, i64, c.c_double, p, p, c.c_int]
     lib.oracle_gemm_cols.restype = None
     lib.oracle_bf16_from_f32.argtypes = [p, i64, p]
+    lib.oracle_fp8_quantize.argtypes = [p, i64, i64, p, p, c.c_int]
+    lib.oracle_fp8_quantize.restype = c.c_int
+    lib.oracle_fp8_gemm_cols.argtypes = [p, i64, i64, p, p, p, i64, p, p, c.c_int]
+    lib.oracle_fp8_gemm_cols.restype = None
     lib.oracle_bf16_from_f32.restype = None
     lib.oracle_glue_scale.argtypes = [p, i64, c.c_float, p]
     lib.oracle_glue_scale.restype = None
@@ -160,6 +164,43 @@ def gemm(a_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray, ts: float = 
     s = np.empty((m, cols.size), np.float64)
     lib.oracle_gemm_cols(_ptr(a), m, k, _ptr(codes), _ptr(scales), _ptr(cols), cols.size,
                          float(ts), _ptr(c), _ptr(s), int(threads))
+    return c, s
+
+
+def fp8_quantize(w: np.ndarray, threads: int = 0):
+    """fp32 w[n, k] -> (E4M3 codes u8[n, k], fp32 row scales[n]) for the FP8 head."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    codes = np.zeros((n, k), np.uint8)
+    scales = np.zeros(n, np.float32)
+    rc = _load().oracle_fp8_quantize(_ptr(w), n, k, _ptr(codes), _ptr(scales), int(threads))
+    if rc == -1:
+        raise ValueError("non-finite weight")
+    if rc != 0:
+        raise ValueError("bad shape")
+    return codes, scales
+
+
+def fp8_gemm(a_bf16: np.ndarray, codes: np.ndarray, row_scales: np.ndarray, cols=None,
+             threads: int = 0):
+    """(C, S) in fp64 for A[m, k] (bf16 bits) against the FP8 head codes[n, k], row_scales[n].
+
+    With ``cols`` given, only those weight rows are evaluated ([m, len(cols)]).
+    """
+    a = np.ascontiguousarray(a_bf16, dtype=np.uint16)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    row_scales = np.ascontiguousarray(row_scales, dtype=np.float32)
+    m, k = a.shape
+    if codes.shape[1] != k or row_scales.shape[0] != codes.shape[0]:
+        raise ValueError("shape mismatch between A and the weights")
+    cols = np.arange(codes.shape[0], dtype=np.int64) if cols is None else \
+        np.ascontiguousarray(cols, dtype=np.int64)
+    if cols.size and (cols.min() < 0 or cols.max() >= codes.shape[0]):
+        raise ValueError("column index out of range")
+    c = np.empty((m, cols.size), np.float64)
+    s = np.empty((m, cols.size), np.float64)
+    _load().oracle_fp8_gemm_cols(_ptr(a), m, k, _ptr(codes), _ptr(row_scales), _ptr(cols),
+                                 cols.size, _ptr(c), _ptr(s), int(threads))
     return c, s
 
 

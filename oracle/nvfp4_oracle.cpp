@@ -285,6 +285,63 @@ void oracle_gemm(const uint16_t *a, int64_t m, int64_t k, const uint8_t *codes,
   oracle_gemm_cols(a, m, k, codes, scales, cols.data(), n, ts, c, s, threads);
 }
 
+// ---- FP8 output head --------------------------------------------------------
+// The served model keeps its output head in FP8 (TandemLLM manual, "What
+// TandemLLM is", 1.2 "Two levers"; "Installing TandemLLM", 3.11 passes it as a
+// separate checkpoint). The pages give neither the FP8 variant nor the scale
+// granularity. The plainest reading, used here: OCP E4M3 codes (the same "FN"
+// format as the NVFP4 block scales) with one fp32 scale per output row:
+//   s(j)     = fp32( absmax_k |w(j,k)| / 448 )     (fp64 division, one rounding)
+//   code     = E4M3_RNE( w(j,k) / s(j) )  (fp64, saturating at 448, sign kept);
+//              every code is +0 when s(j) == 0
+//   w8(j,k)  = s(j) * E4M3(code(j,k))              exact in fp64
+//   C[i][j]  = sum_{k ascending} a(i,k) * w8(j,k)  fp64; S = sum of |terms|
+
+// Quantise fp32 w[n][k] to E4M3 codes[n][k] and fp32 row scales[n]. Returns 0,
+// -1 for a non-finite input, -2 for a bad shape.
+int oracle_fp8_quantize(const float *w, int64_t n, int64_t k, uint8_t *codes, float *row_scales,
+                        int threads) {
+  if (n < 0 || k < 0) return -2;
+  for (int64_t i = 0; i < n * k; ++i)
+    if (!std::isfinite(w[i])) return -1;
+  parallel_rows(n, threads, [&](int64_t j) {
+    const float *wr = w + j * k;
+    double amax = 0.0;
+    for (int64_t kk = 0; kk < k; ++kk) amax = std::fmax(amax, std::fabs((double)wr[kk]));
+    const float s = (float)(amax / 448.0);
+    row_scales[j] = s;
+    for (int64_t kk = 0; kk < k; ++kk)
+      codes[j * k + kk] = (s == 0.0f) ? 0 : e4m3_encode((double)wr[kk] / (double)s);
+  });
+  return 0;
+}
+
+// C[i][c], S[i][c] (m x ncols, row-major) for the weight rows cols[0..ncols)
+// of the FP8 head: codes[n][k], row_scales[n]; a is m x k bf16, row-major.
+void oracle_fp8_gemm_cols(const uint16_t *a, int64_t m, int64_t k, const uint8_t *codes,
+                          const float *row_scales, const int64_t *cols, int64_t ncols,
+                          double *c, double *s, int threads) {
+  std::vector<double> av((size_t)(m * k));
+  for (int64_t i = 0; i < m * k; ++i) av[(size_t)i] = bf16_value(a[i]);
+  parallel_rows(ncols, threads, [&](int64_t idx) {
+    const int64_t j = cols[idx];
+    const double sj = (double)row_scales[j];
+    std::vector<double> w((size_t)k);
+    for (int64_t kk = 0; kk < k; ++kk) w[(size_t)kk] = sj * e4m3_value(codes[j * k + kk]);
+    for (int64_t i = 0; i < m; ++i) {
+      const double *ar = av.data() + i * k;
+      double acc = 0.0, sacc = 0.0;
+      for (int64_t kk = 0; kk < k; ++kk) {
+        const double p = ar[kk] * w[(size_t)kk];
+        acc += p;
+        sacc += std::fabs(p);
+      }
+      c[i * ncols + idx] = acc;
+      if (s) s[i * ncols + idx] = sacc;
+    }
+  });
+}
+
 // fp32 -> bf16, round to nearest even (NaN stays NaN).
 void oracle_bf16_from_f32(const float *x, int64_t count, uint16_t *out) {
   for (int64_t i = 0; i < count; ++i) out[i] = bf16_from_float_rne(x[i]);

@@ -130,3 +130,14 @@ def weights_f32_cuda(n: int, k: int, seed: int = 0, stream: str = "w", out=None)
         out = torch.empty((n, k), dtype=torch.float32, device="cuda")
     out.normal_(0.0, 1.0, generator=g)
     return out
+
+
+def fp8_codes(n: int, k: int, seed: int = 0, stream: str = "fp8") -> np.ndarray:
+    """Uniformly random finite OCP E4M3 bytes u8[n, k] (0x7F and 0xFF, the NaNs, excluded)."""
+    r = rng(seed, stream, n, k).integers(0, 254, size=(n, k), dtype=np.uint8)
+    return r + (r >= 0x7F).astype(np.uint8)
+
+
+def fp8_row_scales(n: int, seed: int = 0, stream: str = "fp8s") -> np.ndarray:
+    """fp32 row scales [n] spread over 2^-14 .. 2^-6 (|w| / 448 for weights of a few 1e-3 to 1e-1)."""
+    return np.exp2(rng(seed, stream, n).uniform(-14.0, -6.0, size=n)).astype(np.float32)
