@@ -289,6 +289,36 @@ def staircase_report(ctx, m_hi=64, reps=7):
     return out
 
 
+def fp8_head_report(torch, nv, synth, ctx, ms=(1, 8, 16, 24, 32), warmup=3, reps=20):
+    """The FP8 output head (151936 x 5120 E4M3 codes + fp32 row scales, the
+    step after the last layer): microseconds per launch and weight GB/s at the
+    tree sizes. Random finite codes; the 778 MB of weights exceed every cache,
+    so back-to-back launches stream them from HBM."""
+    n, k = 151936, 5120
+    packed = torch.from_numpy(nv.fp8_pack_host(synth.fp8_codes(n, k, seed=1),
+                                               synth.fp8_row_scales(n, seed=1))).cuda()
+    wbytes = n * k + n * 4
+    out = {"shape": [n, k], "weight_bytes": wbytes, "us": {}, "GBps": {}}
+    for m in ms:
+        a = torch.from_numpy(synth.activations_bf16(m, k, seed=m, stream="headbench").view("int16")).cuda().view(torch.bfloat16)
+        c = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        for _ in range(warmup):
+            ctx.fp8_head_gemm(a, packed, n, k, out=c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            ctx.fp8_head_gemm(a, packed, n, k, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out["us"][str(m)] = round(us, 2)
+        out["GBps"][str(m)] = round(wbytes / (us * 1e-6) / 1e9, 1)
+    log("fp8 head [%dx%d]: %s us; %s GB/s" % (n, k, out["us"], out["GBps"]))
+    del packed
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +332,7 @@ def main():
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-staircase", action="store_true")
+    ap.add_argument("--no-head", action="store_true", help="skip the FP8 output head timing")
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the verify-GEMM roofline leg and a 256 MiB copy (for hardware-counter runs)")
     args = ap.parse_args()
@@ -398,6 +429,7 @@ def main():
         achieved, 100 * achieved / PEAK_HBM_GBS, ceiling))
 
     stair = None if args.no_staircase else staircase_report(ctx)
+    head = None if args.no_head else fp8_head_report(torch, nv, synth, ctx)
 
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
@@ -415,6 +447,7 @@ def main():
         "roofline": roofline,
         "read_ceiling_GBps": round(ceiling, 1),
         "staircase": stair,
+        "fp8_head": head,
         "pages_context": PAGES_CONTEXT,
     }
     if not args.no_cpu_baseline:

@@ -168,6 +168,40 @@ int nvfp4v_verify_gemm_pa(nvfp4v_ctx *ctx, const void *act_dev, int64_t m, int64
                           const void *packed_dev, int64_t n, float ts, float *c_dev,
                           hipStream_t stream);
 
+/* ---- The FP8 output head ------------------------------------------------ */
+
+/* The output head applied after the last layer of a verify pass: the served
+ * model keeps it in FP8 (TandemLLM manual, "What TandemLLM is", 1.2 "Two
+ * levers"). The pages give neither the FP8 variant nor the scale granularity;
+ * read here as OCP E4M3 ("FN") codes with one fp32 scale per weight row:
+ *   s(j) = fp32(absmax_k |w(j,k)| / 448), code = E4M3_RNE(w / s) saturating at
+ *   448 with the sign kept (every code +0 when s(j) == 0).
+ *   nvfp4v_fp8_packed_bytes: bytes of the packed head for N x K (0 if N < 1,
+ *     K < 16, K % 16 != 0, N > 2^28 or K > 2^22).
+ *   nvfp4v_fp8_quantize_host: fp32 w[N][K] (host) -> codes u8[N][K] row-major
+ *     and row_scales fp32[N] (host, caller-owned). Errors: INVALID_ARG, SHAPE,
+ *     NONFINITE (NaN or Inf in w).
+ *   nvfp4v_fp8_pack_host: codes + row scales (host) -> the packed layout in a
+ *     caller-owned host buffer of nvfp4v_fp8_packed_bytes bytes (copy it to the
+ *     device once; offline). Errors: INVALID_ARG, SHAPE.
+ *   nvfp4v_fp8_head_gemm: C[M][N] fp32 = A[M][K] * (s . W8)^T for bf16 A
+ *     (device, row-major, 16-byte aligned), the packed head (device, 16-byte
+ *     aligned), C (device, row-major, 16-byte aligned, fully overwritten).
+ *     M in 1..32. A is packed into the context's buffer first (two kernels).
+ *     Does not allocate. Errors: INVALID_ARG, M_RANGE, SHAPE, ALIGN, WORKSPACE,
+ *     HIP, FAULT.
+ *   nvfp4v_fp8_head_gemm_pa: the same with A given packed
+ *     (nvfp4v_pack_activations). */
+size_t nvfp4v_fp8_packed_bytes(int64_t n, int64_t k);
+int nvfp4v_fp8_quantize_host(const float *w_host, int64_t n, int64_t k, uint8_t *codes_host,
+                             float *row_scales_host);
+int nvfp4v_fp8_pack_host(const uint8_t *codes_host, const float *row_scales_host, int64_t n,
+                         int64_t k, void *packed_host);
+int nvfp4v_fp8_head_gemm(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_t k,
+                         const void *packed_dev, int64_t n, float *c_dev, hipStream_t stream);
+int nvfp4v_fp8_head_gemm_pa(nvfp4v_ctx *ctx, const void *act_dev, int64_t m, int64_t k,
+                            const void *packed_dev, int64_t n, float *c_dev, hipStream_t stream);
+
 /* The kernel variant and tiling the tile table picks for (N, K, M): writes a
  * short description into buf (NUL-terminated, truncated to len). */
 int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64_t m, char *buf, size_t len);

@@ -89,6 +89,12 @@ def load():
     lib.nvfp4v_read_probe_sink_words.restype = c.c_size_t
     lib.nvfp4v_read_probe.argtypes = [p, p, c.c_size_t, p, p]
     lib.nvfp4v_copy_probe.argtypes = [p, p, p, c.c_size_t, p]
+    lib.nvfp4v_fp8_packed_bytes.argtypes = [i64, i64]
+    lib.nvfp4v_fp8_packed_bytes.restype = c.c_size_t
+    lib.nvfp4v_fp8_quantize_host.argtypes = [p, i64, i64, p, p]
+    lib.nvfp4v_fp8_pack_host.argtypes = [p, p, i64, i64, p]
+    lib.nvfp4v_fp8_head_gemm.argtypes = [p, p, i64, i64, p, i64, p, p]
+    lib.nvfp4v_fp8_head_gemm_pa.argtypes = [p, p, i64, i64, p, i64, p, p]
     _lib = lib
     return lib
 
@@ -146,6 +152,39 @@ def encode_e4m3_host(x):
     out = np.zeros(x.shape, np.uint8)
     _check(load().nvfp4v_encode_e4m3_host(_np_ptr(x), x.size, _np_ptr(out)),
            "nvfp4v_encode_e4m3_host")
+    return out
+
+
+def fp8_packed_bytes(n: int, k: int) -> int:
+    return int(load().nvfp4v_fp8_packed_bytes(int(n), int(k)))
+
+
+def fp8_quantize_host(w):
+    """fp32 numpy w[n, k] -> (E4M3 codes u8[n, k], fp32 row scales[n]) for the FP8 head."""
+    import numpy as np
+
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    codes = np.zeros((n, k), np.uint8)
+    scales = np.zeros(n, np.float32)
+    _check(load().nvfp4v_fp8_quantize_host(_np_ptr(w), n, k, _np_ptr(codes), _np_ptr(scales)),
+           "nvfp4v_fp8_quantize_host")
+    return codes, scales
+
+
+def fp8_pack_host(codes, row_scales):
+    """E4M3 codes u8[n, k] + fp32 row scales[n] -> packed head (host uint8 array)."""
+    import numpy as np
+
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    row_scales = np.ascontiguousarray(row_scales, dtype=np.float32)
+    n, k = codes.shape
+    nb = fp8_packed_bytes(n, k)
+    if nb == 0 or row_scales.shape != (n,):
+        raise Nvfp4vError(E_SHAPE, "fp8_pack_host")
+    out = np.empty(nb, np.uint8)
+    _check(load().nvfp4v_fp8_pack_host(_np_ptr(codes), _np_ptr(row_scales), n, k, _np_ptr(out)),
+           "nvfp4v_fp8_pack_host")
     return out
 
 
@@ -246,6 +285,29 @@ class Context:
         _check(load().nvfp4v_verify_gemm_pa(self._h, _t_ptr(act), m, k, _t_ptr(packed), n,
                                             float(ts), _t_ptr(out), _stream_handle(stream)),
                "nvfp4v_verify_gemm_pa")
+        return out
+
+    def fp8_head_gemm(self, a, packed, n: int, k: int, out=None, stream=None):
+        """C[m, n] fp32 = A[m, k] (bf16 cuda tensor) * (s . W8)^T for the packed FP8 head."""
+        import torch
+
+        m = a.shape[0]
+        if out is None:
+            out = torch.empty((m, n), dtype=torch.float32, device=a.device)
+        _check(load().nvfp4v_fp8_head_gemm(self._h, _t_ptr(a), m, k, _t_ptr(packed), n,
+                                           _t_ptr(out), _stream_handle(stream)),
+               "nvfp4v_fp8_head_gemm")
+        return out
+
+    def fp8_head_gemm_pa(self, act, m: int, k: int, packed, n: int, out=None, stream=None):
+        """fp8_head_gemm with activations already packed by pack_activations."""
+        import torch
+
+        if out is None:
+            out = torch.empty((m, n), dtype=torch.float32, device=act.device)
+        _check(load().nvfp4v_fp8_head_gemm_pa(self._h, _t_ptr(act), m, k, _t_ptr(packed), n,
+                                              _t_ptr(out), _stream_handle(stream)),
+               "nvfp4v_fp8_head_gemm_pa")
         return out
 
     # -- chain glue and the full pass ---------------------------------------

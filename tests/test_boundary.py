@@ -169,3 +169,47 @@ def test_host_e4m3_encoder_matches_oracle(oracle_mod):
     assert np.array_equal(got, ref)
     with pytest.raises(nv.Nvfp4vError):
         nv.encode_e4m3_host(np.float32([1.0, np.nan]))
+
+
+def test_fp8_host_quantiser_matches_oracle(oracle_mod):
+    w = synth.weights_f32(37, 272, seed=11, stream="fp8q")
+    w[3] = 0.0
+    w[5, 7] = -w[5].__abs__().max() * 2
+    codes, scales = nv.fp8_quantize_host(w)
+    oc, os_ = oracle_mod.fp8_quantize(w)
+    assert np.array_equal(codes, oc)
+    assert np.array_equal(scales.view(np.uint32), os_.view(np.uint32))
+    w[1, 1] = np.nan
+    with pytest.raises(nv.Nvfp4vError):
+        nv.fp8_quantize_host(w)
+
+
+def test_fp8_pack_layout():
+    """The packed head re-read with the layout the header states: 16-row x 256-k
+    tiles of 4096 bytes; load p, lane r + 16 h holds row r, k = 64 h + 16 p + b;
+    then fp32 row scales padded to whole row tiles."""
+    n, k = 37, 784
+    codes = synth.fp8_codes(n, k, seed=2)
+    scales = synth.fp8_row_scales(n, seed=2)
+    packed = nv.fp8_pack_host(codes, scales)
+    nrt, nkt = (n + 15) // 16, (k + 255) // 256
+    assert packed.size == nv.fp8_packed_bytes(n, k) == nrt * nkt * 4096 + nrt * 64
+    t = packed[:nrt * nkt * 4096].reshape(nrt, nkt, 4, 4, 16, 16)  # rt, kt, p, h, r, b
+    full = np.zeros((nrt * 16, nkt * 256), np.uint8)
+    for rt in range(nrt):
+        for kt in range(nkt):
+            blk = t[rt, kt].transpose(2, 1, 0, 3).reshape(16, 256)  # r, (h, p, b)
+            full[rt * 16:(rt + 1) * 16, kt * 256:(kt + 1) * 256] = blk
+    assert np.array_equal(full[:n, :k], codes)
+    assert not full[n:].any() and not full[:, k:].any()
+    sc = packed[nrt * nkt * 4096:].view(np.float32)
+    assert np.array_equal(sc[:n], scales) and not sc[n:].any()
+
+
+def test_fp8_head_argument_errors(lib):
+    assert nv.fp8_packed_bytes(0, 16) == 0 and nv.fp8_packed_bytes(4, 24) == 0
+    assert nv.fp8_packed_bytes(1, 16) == 4096 + 64
+    assert lib.nvfp4v_fp8_head_gemm(None, None, 1, 16, None, 1, None, None) == nv.E_INVALID_ARG
+    assert lib.nvfp4v_fp8_head_gemm_pa(None, None, 1, 16, None, 1, None, None) == nv.E_INVALID_ARG
+    with pytest.raises(nv.Nvfp4vError):
+        nv.fp8_pack_host(np.zeros((2, 24), np.uint8), np.zeros(2, np.float32))
