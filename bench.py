@@ -333,6 +333,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-staircase", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip the FP8 output head timing")
+    ap.add_argument("--head-only", action="store_true", help="time only the FP8 output head")
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the verify-GEMM roofline leg and a 256 MiB copy (for hardware-counter runs)")
     args = ap.parse_args()
@@ -351,6 +352,10 @@ def main():
     ctx = nv.Context(0)
     layers = args.layers
     log("device: %s, %d layers" % (torch.cuda.get_device_name(0), layers))
+    if args.head_only:
+        print(json.dumps({"fp8_head": fp8_head_report(torch, nv, synth, ctx)}), flush=True)
+        ctx.close()
+        return
     packed = build_stack(torch, nv, synth, ctx, layers)
 
     if args.gemm_only:
