@@ -218,6 +218,28 @@ def cpu_baseline(target_s=12.0, m=16, rows=512):
                       "repetitions, %.1f s; weight+scale bytes per second" % (m, rows, reps, total_t)}
 
 
+def check_device(ctx, nv, what):
+    """A timed leg counts only if every split-K row block of it completed (its
+    pieces met on one XCD); the library reports anything else here."""
+    st = ctx.device_status()
+    assert st == nv.OK, "%s: device status %d (%s)" % (what, st, nv.strerror(st))
+
+
+def teardown(torch, ctx, *holders):
+    """Synchronise, drop the caller's device tensors, return the caching
+    allocator's memory, then destroy the context, in that order."""
+    import gc
+
+    torch.cuda.synchronize()
+    for h in holders:
+        h.clear()
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    ctx.close()
+    torch.cuda.synchronize()
+
+
 def kernel_source_hash():
     """sha256 over the verify GEMM's device sources (the traffic figure in
     profiles/ is valid only for the kernel it was taken on)."""
@@ -394,7 +416,9 @@ def main():
             runner = DirectPass(torch, ctx, layer_arr, h0, ws, h_out, m)
         sec = time_graph(torch, runner, warmup, steps)
         assert ctx.pass_status() == nv.OK, "persistent pass timed out"
+        check_device(ctx, nv, "pass M=%d" % m)
         del runner
+        torch.cuda.synchronize()
         return sec, launch
 
     # ---- headline: the pass at M = args.m --------------------------------------
@@ -421,6 +445,7 @@ def main():
 
     # ---- roofline of the dominant kernel (the verify GEMM), HIP events ----------
     gbytes, gms, launches, per_shape = gemm_event_timing(torch, ctx, packed, args.m)
+    check_device(ctx, nv, "roofline GEMMs")
     achieved = gbytes / (gms * 1e-3) / 1e9
     traffic = traffic_from_profile(kernel_source_hash())
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -434,7 +459,9 @@ def main():
         achieved, 100 * achieved / PEAK_HBM_GBS, ceiling))
 
     stair = None if args.no_staircase else staircase_report(ctx)
+    check_device(ctx, nv, "staircase")
     head = None if args.no_head else fp8_head_report(torch, nv, synth, ctx)
+    check_device(ctx, nv, "fp8 head")
 
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
@@ -455,10 +482,13 @@ def main():
         "fp8_head": head,
         "pages_context": PAGES_CONTEXT,
     }
+    # Release every device object (weights, workspace, the context) before the
+    # interpreter exits, so nothing of the run is torn down by late destructors.
+    del layer_arr, h0, ws, h_out
+    teardown(torch, ctx, packed)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(m=args.m)
     print(json.dumps(result), flush=True)
-    ctx.close()
 
 
 if __name__ == "__main__":

@@ -93,6 +93,11 @@ void nvfp4v_destroy(nvfp4v_ctx *ctx);
  * Errors: INVALID_ARG, HIP. */
 int nvfp4v_device_status(nvfp4v_ctx *ctx);
 
+/* Size in bytes of the opaque context object. Host-only tests use it to build a
+ * zeroed stand-in context whose every argument check runs on the host and
+ * returns before any HIP call (an all-zero context has an empty workspace). */
+size_t nvfp4v_ctx_size(void);
+
 /* Human-readable text for a status code (static storage). */
 const char *nvfp4v_strerror(int status);
 /* The hipError_t behind the last NVFP4V_E_HIP on this context (0 if none). */

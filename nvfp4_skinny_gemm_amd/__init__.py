@@ -59,6 +59,8 @@ def load():
     lib.nvfp4v_strerror.argtypes = [c.c_int]
     lib.nvfp4v_strerror.restype = c.c_char_p
     lib.nvfp4v_last_hip_error.argtypes = [p]
+    lib.nvfp4v_ctx_size.argtypes = []
+    lib.nvfp4v_ctx_size.restype = c.c_size_t
     lib.nvfp4v_device_status.argtypes = [p]
     lib.nvfp4v_quantize_host.argtypes = [p, i64, i64, p, p]
     lib.nvfp4v_quantize.argtypes = [p, p, i64, i64, p, p, p]
@@ -122,6 +124,50 @@ def _stream_handle(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _require(t, name, dtypes=None, shape=None, min_bytes=None):
+    """Check a device tensor before its address crosses the C ABI: a CUDA
+    tensor, contiguous, of one of `dtypes`, of exactly `shape`, and holding at
+    least `min_bytes` bytes. The library checks pointers and sizes it is given;
+    this checks that the tensor really is what those sizes describe."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor, got %s" % (name, type(t).__name__))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device (cuda) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError("%s must have dtype %s, got %s" % (name, " or ".join(map(str, dtypes)), t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if min_bytes is not None and _nbytes(t) < min_bytes:
+        raise ValueError("%s holds %d bytes, needs at least %d" % (name, _nbytes(t), min_bytes))
+    return t
+
+
+def _bf16_types():
+    import torch
+
+    return (torch.bfloat16, torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.bfloat16, torch.int16)
+
+
+def _f32():
+    import torch
+
+    return (torch.float32,)
+
+
+def _u8():
+    import torch
+
+    return (torch.uint8,)
 
 
 def packed_bytes(n: int, k: int) -> int:
@@ -225,6 +271,7 @@ class Context:
         """fp32 cuda tensor w[n, k] -> (codes u8[n, k/2], scales u8[n, k/16]) on the device."""
         import torch
 
+        _require(w, "w", _f32())
         n, k = w.shape
         codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
         scales = torch.empty((n, k // 16), dtype=torch.uint8, device=w.device)
@@ -236,8 +283,11 @@ class Context:
         import torch
 
         nb = packed_bytes(n, k)
+        _require(codes, "codes", _u8(), min_bytes=n * (k // 2))
+        _require(scales, "scales", _u8(), min_bytes=n * (k // 16))
         if out is None:
             out = torch.empty(nb, dtype=torch.uint8, device=codes.device)
+        _require(out, "out", min_bytes=nb)
         _check(load().nvfp4v_pack(self._h, _t_ptr(codes), _t_ptr(scales), n, k, _t_ptr(out),
                                   _stream_handle(stream)), "nvfp4v_pack")
         return out
@@ -245,6 +295,7 @@ class Context:
     def unpack(self, packed, n: int, k: int, stream=None):
         import torch
 
+        _require(packed, "packed", min_bytes=packed_bytes(n, k))
         codes = torch.empty((n, k // 2), dtype=torch.uint8, device=packed.device)
         scales = torch.empty((n, k // 16), dtype=torch.uint8, device=packed.device)
         _check(load().nvfp4v_unpack(self._h, _t_ptr(packed), n, k, _t_ptr(codes), _t_ptr(scales),
@@ -257,8 +308,11 @@ class Context:
         import torch
 
         m = a.shape[0]
+        _require(a, "a", _bf16_types(), shape=(m, k))
+        _require(packed, "packed", min_bytes=packed_bytes(n, k))
         if out is None:
             out = torch.empty((m, n), dtype=torch.float32, device=a.device)
+        _require(out, "out", _f32(), shape=(m, n))
         _check(load().nvfp4v_verify_gemm(self._h, _t_ptr(a), m, k, _t_ptr(packed), n,
                                          float(ts), _t_ptr(out), _stream_handle(stream)),
                "nvfp4v_verify_gemm")
@@ -268,9 +322,11 @@ class Context:
         """bf16 cuda tensor a[m, k] -> packed activations (uint8 cuda tensor)."""
         import torch
 
+        _require(a, "a", _bf16_types())
         m, k = a.shape
         if out is None:
             out = torch.empty(act_packed_bytes(m, k), dtype=torch.uint8, device=a.device)
+        _require(out, "out", min_bytes=act_packed_bytes(m, k))
         _check(load().nvfp4v_pack_activations(self._h, _t_ptr(a), m, k, _t_ptr(out),
                                               _stream_handle(stream)), "nvfp4v_pack_activations")
         return out
@@ -280,8 +336,11 @@ class Context:
         """verify_gemm with activations already packed by pack_activations."""
         import torch
 
+        _require(act, "act", min_bytes=act_packed_bytes(m, k))
+        _require(packed, "packed", min_bytes=packed_bytes(n, k))
         if out is None:
             out = torch.empty((m, n), dtype=torch.float32, device=act.device)
+        _require(out, "out", _f32(), shape=(m, n))
         _check(load().nvfp4v_verify_gemm_pa(self._h, _t_ptr(act), m, k, _t_ptr(packed), n,
                                             float(ts), _t_ptr(out), _stream_handle(stream)),
                "nvfp4v_verify_gemm_pa")
@@ -292,8 +351,11 @@ class Context:
         import torch
 
         m = a.shape[0]
+        _require(a, "a", _bf16_types(), shape=(m, k))
+        _require(packed, "packed", min_bytes=fp8_packed_bytes(n, k))
         if out is None:
             out = torch.empty((m, n), dtype=torch.float32, device=a.device)
+        _require(out, "out", _f32(), shape=(m, n))
         _check(load().nvfp4v_fp8_head_gemm(self._h, _t_ptr(a), m, k, _t_ptr(packed), n,
                                            _t_ptr(out), _stream_handle(stream)),
                "nvfp4v_fp8_head_gemm")
@@ -303,8 +365,11 @@ class Context:
         """fp8_head_gemm with activations already packed by pack_activations."""
         import torch
 
+        _require(act, "act", min_bytes=act_packed_bytes(m, k))
+        _require(packed, "packed", min_bytes=fp8_packed_bytes(n, k))
         if out is None:
             out = torch.empty((m, n), dtype=torch.float32, device=act.device)
+        _require(out, "out", _f32(), shape=(m, n))
         _check(load().nvfp4v_fp8_head_gemm_pa(self._h, _t_ptr(act), m, k, _t_ptr(packed), n,
                                               _t_ptr(out), _stream_handle(stream)),
                "nvfp4v_fp8_head_gemm_pa")
@@ -315,9 +380,12 @@ class Context:
         """bf16(x * c) for an fp32 cuda tensor x[rows, cols] (row stride x.stride(0))."""
         import torch
 
+        if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1 or not x.is_cuda:
+            raise ValueError("x must be a 2-D fp32 cuda tensor with unit column stride")
         rows, cols = x.shape
         if out is None:
             out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+        _require(out, "out", _bf16_types(), shape=(rows, cols))
         _check(load().nvfp4v_glue_scale(self._h, _t_ptr(x), x.stride(0), rows, cols, float(c),
                                         _t_ptr(out), _stream_handle(stream)), "nvfp4v_glue_scale")
         return out
@@ -326,9 +394,15 @@ class Context:
         """bf16(x * c + y * c) for fp32 cuda tensors of one shape (no fused multiply-add)."""
         import torch
 
+        for t, nm in ((x, "x"), (y, "y")):
+            if t.dtype != torch.float32 or t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda:
+                raise ValueError("%s must be a 2-D fp32 cuda tensor with unit column stride" % nm)
+        if tuple(y.shape) != tuple(x.shape):
+            raise ValueError("x and y must have one shape")
         rows, cols = x.shape
         if out is None:
             out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+        _require(out, "out", _bf16_types(), shape=(rows, cols))
         _check(load().nvfp4v_glue_sum(self._h, _t_ptr(x), x.stride(0), _t_ptr(y), y.stride(0),
                                       rows, cols, float(c), _t_ptr(out), _stream_handle(stream)),
                "nvfp4v_glue_sum")
@@ -338,6 +412,11 @@ class Context:
                     stream=None):
         """Enqueue the chained pass; layers is a ctypes array of Layer."""
         m = h0.shape[0]
+        _require(h0, "h0", _bf16_types(), shape=(m, hidden))
+        _require(h_out, "h_out", _bf16_types(), shape=(m, hidden))
+        _require(ws, "ws", min_bytes=pass_workspace_bytes(m, hidden, inter, len(layers)))
+        if trace is not None:
+            _require(trace, "trace", _bf16_types(), shape=(len(layers), m, hidden))
         _check(load().nvfp4v_verify_pass(
             self._h, ctypes.cast(layers, ctypes.c_void_p), len(layers), hidden, inter,
             _t_ptr(h0), m, _t_ptr(ws), ws.numel() * ws.element_size(), _t_ptr(h_out),

@@ -109,6 +109,8 @@ extern "C" int nvfp4v_device_status(nvfp4v_ctx *ctx) {
   return NVFP4V_E_DISPATCH;
 }
 
+extern "C" size_t nvfp4v_ctx_size(void) { return sizeof(nvfp4v_ctx); }
+
 extern "C" int nvfp4v_last_hip_error(const nvfp4v_ctx *ctx) { return ctx ? ctx->last_hip : 0; }
 
 extern "C" int nvfp4v_set_pass_mode(nvfp4v_ctx *ctx, int mode) {

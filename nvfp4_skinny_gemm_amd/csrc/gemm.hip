@@ -28,12 +28,19 @@
 //  * v_mfma_f32_16x16x32_bf16 with the weights as the 16-row A operand and a
 //    16-row block of activations as the B operand, fp32 accumulation.
 //  * The 4 waves' tiles are summed through LDS in wave order. With ksplit > 1
-//    every work-group stores its partial tile with system-coherent stores
-//    (they bypass the non-coherent L2s of the other dies, so no L2 write-back
-//    fence is needed), waits for them, and takes an arrival ticket; the last
-//    work-group to arrive sums the partials in split order 0..ksplit-1. Both
-//    orders are fixed, so C is bitwise reproducible (TandemLLM manual, 1.7 "The
-//    paper": the 4-bit kernels keep a fixed reduction order). No float atomics.
+//    the K pieces of a row block exchange partial tiles. By default (the
+//    create-time dispatch probe found that work-groups with linear ids
+//    congruent mod 8 run on one XCD, and the grid's x is padded to a multiple
+//    of 8) they meet in that XCD's L2: plain stores, a ticket atomic executed
+//    in the L2, loads that read through the L1. In the register variant the
+//    last piece to take a ticket sums the partials; in the LDS variant the
+//    row block's last piece is a designated reducer that keeps its own
+//    partial in LDS and waits for its siblings. Otherwise (or with
+//    NVFP4V_SPLITK_EXCHANGE=memory) they meet in memory: system-coherent
+//    stores, ticket and loads, and the last arriver sums. Every path sums in
+//    split order 0..ksplit-1, so C is bitwise reproducible and the two
+//    exchanges agree bitwise (TandemLLM manual, 1.7 "The paper": the 4-bit
+//    kernels keep a fixed reduction order). No float atomics.
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>

@@ -40,24 +40,22 @@ def test_packed_bytes():
     assert nv.packed_bytes(16, 40) == 0
 
 
-class _CtxFields(ctypes.Structure):
-    # mirrors the leading fields of struct nvfp4v_ctx (csrc/internal.h)
-    _fields_ = [("device", ctypes.c_int), ("num_cus", ctypes.c_int), ("last_hip", ctypes.c_int),
-                ("partials", ctypes.c_void_p), ("partial_floats", ctypes.c_size_t),
-                ("counters", ctypes.c_void_p), ("n_counters", ctypes.c_size_t)]
-
-
 _KEEP = []
 
 
 class FakeCtx:
-    """A host block standing in for a context with an empty workspace and 256 CUs:
-    every call made with it must return from its host-side checks, before any
-    HIP call. Kept alive for the whole module."""
+    """A zeroed host block of the full size of struct nvfp4v_ctx (empty
+    workspace, no device buffers) with its CU count set to 256: every call made
+    with it must return from its host-side checks, before any HIP call. Kept
+    alive for the whole module."""
 
     def __init__(self):
-        self.fields = _CtxFields(0, 256, 0, None, 0, None, 0)
-        self.ptr = ctypes.cast(ctypes.pointer(self.fields), ctypes.c_void_p)
+        size = int(nv.load().nvfp4v_ctx_size())
+        assert size >= 64
+        self.buf = ctypes.create_string_buffer(size)  # zero-filled
+        # leading fields of the struct: int device, int num_cus
+        ctypes.c_int.from_buffer(self.buf, 4).value = 256
+        self.ptr = ctypes.cast(self.buf, ctypes.c_void_p)
         _KEEP.append(self)
 
 

@@ -220,7 +220,9 @@ def test_lm_head_sampled(torch_cuda, ctx, oracle_mod):
     a = synth.activations_bf16(64, k, seed=0, stream="head/act", outliers=True)
     c_ref, s_ref = oracle_mod.gemm(a, oc, osc)
     a_dev = bf16_dev(torch, a)
-    for m in (1, 16, 17, 32, 64):
+    # every tile-table regime of the head: one row block (LDS-staged, R = 2),
+    # two, three (33..48) and four row blocks
+    for m in (1, 16, 17, 32, 33, 40, 48, 64):
         log("head M=%d plan: %s" % (m, ctx.describe_plan(n, k, m)))
         c = ctx.verify_gemm(a_dev[:m], packed, n, k)
         assert_parity(oracle_mod, c[:, idx].cpu().numpy(), c_ref[:m], s_ref[:m], "head M=%d" % m)

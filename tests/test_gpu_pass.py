@@ -205,10 +205,10 @@ def test_graph_replays_equal_eager(torch_cuda, mode_ctx):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("m", [8, 16, 24])
+@pytest.mark.parametrize("m", [8, 16, 24, 32])
 def test_graph_replays_equal_eager_full_size(torch_cuda, ctx, m):
     """Full-size layers in the chained schedule, whose tile table splits K at
-    these row counts (down at 8; gate|up and down at 16; down at 24) and
+    these row counts (down at 8; gate|up and down at 16; down at 24 and 32) and
     exchanges the partial sums through one XCD's L2: graph replays equal the
     eager pass bitwise, with split eager GEMMs on the same context in between
     (they share the arrival counters), and no row block reports pieces on two
@@ -283,7 +283,7 @@ def workspace_views(ws, m, H, I, L):
 
 
 @pytest.mark.parametrize("mode_ctx", ALL_MODES, indirect=True)
-@pytest.mark.parametrize("m", [16, 24])
+@pytest.mark.parametrize("m", [16, 24, 32])
 def test_full_size_phases_against_oracle(torch_cuda, mode_ctx, oracle_mod, m):
     """Two full-size layers (H = 5120, I = 17408). For the last layer, every
     GEMM's fp32 output is checked against the oracle on 384 sampled weight
