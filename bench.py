@@ -33,6 +33,9 @@ H, I, LAYERS = 5120, 17408, 64
 BYTES_PER_WEIGHT = 0.5625  # 4-bit code + one E4M3 byte per 16 weights
 PEAK_HBM_GBS = 8000.0
 METRIC = "verify-pass µs and achieved HBM GB/s vs M (1..32), full 27B layer stack"
+# Pass schedules (nvfp4v_set_pass_mode) by name.
+SCHEDULES = {"chain": "PASS_CHAIN", "persistent": "PASS_PERSISTENT", "flow": "PASS_FLOW",
+             "stream": "PASS_STREAM"}
 PAGES_CONTEXT = {"hardware": "DGX Spark GB10 (other machine; whole forward pass incl. attention)",
                  "verify_pass_ms": {"8": 75.5, "16": 74.4, "24": 83.1, "32": 87.8}}
 
@@ -347,8 +350,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--m", type=int, default=16)
-    ap.add_argument("--mode", choices=("chain", "persistent"), default="chain",
-                    help="pass schedule of the headline number (the other is reported beside it)")
+    ap.add_argument("--mode", choices=tuple(SCHEDULES), default="chain",
+                    help="pass schedule of the headline number")
+    ap.add_argument("--compare", default="stream",
+                    help="comma-separated schedules timed beside the headline one ('' = none)")
     ap.add_argument("--sweep", default="1-32", help="M values for the per-M pass staircase ('' = none)")
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--layers", type=int, default=LAYERS)
@@ -403,8 +408,10 @@ def main():
     ws = torch.empty(nv.pass_workspace_bytes(64, H, I, layers), dtype=torch.uint8, device="cuda")
     h_out = torch.empty((64, H), dtype=torch.bfloat16, device="cuda")
     pass_bytes = layer_weight_bytes() * layers
-    modes = {"chain": nv.PASS_CHAIN, "persistent": nv.PASS_PERSISTENT}
-    other = "persistent" if args.mode == "chain" else "chain"
+    modes = {name: getattr(nv, const) for name, const in SCHEDULES.items()}
+    others = [o for o in args.compare.split(",") if o and o != args.mode]
+    for o in others:
+        assert o in modes, "unknown schedule %r" % o
 
     def timed_pass(m, warmup, steps):
         launch = "graph"
@@ -425,14 +432,17 @@ def main():
     # One step is one pass over all layers: a packing kernel plus the layers'
     # GEMMs (four launches per layer, or one persistent kernel per 32 layers),
     # replayed from a HIP graph; weights and input are resident in HBM.
-    ctx.set_pass_mode(modes[other])
-    sec_other, _ = timed_pass(args.m, 2, max(3, args.steps // 4))
+    sec_others = {}
+    for o in others:
+        ctx.set_pass_mode(modes[o])
+        sec_others[o], _ = timed_pass(args.m, 2, max(3, args.steps // 4))
     ctx.set_pass_mode(modes[args.mode])
     sec, launch = timed_pass(args.m, args.warmup, args.steps)
     assert torch.isfinite(h_out[: args.m].float()).all(), "non-finite pass output"
     gbs = pass_bytes / sec / 1e9
-    log("M=%d: %.1f us per pass, %.1f GB/s (%s, %s); %s schedule %.1f us" % (
-        args.m, sec * 1e6, gbs, args.mode, launch, other, sec_other * 1e6))
+    log("M=%d: %.1f us per pass, %.1f GB/s (%s, %s); %s" % (
+        args.m, sec * 1e6, gbs, args.mode, launch,
+        ", ".join("%s %.1f us" % (o, t * 1e6) for o, t in sec_others.items())))
 
     # ---- per-M staircase of the pass ------------------------------------------
     per_m = {}
@@ -474,7 +484,7 @@ def main():
                    "schedule": args.mode, "launch": launch},
         "pass_us": round(sec * 1e6, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-        "pass_us_%s" % other: round(sec_other * 1e6, 1),
+        "pass_us_other_schedules": {o: round(t * 1e6, 1) for o, t in sec_others.items()},
         "per_m": per_m,
         "roofline": roofline,
         "read_ceiling_GBps": round(ceiling, 1),

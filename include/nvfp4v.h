@@ -227,6 +227,45 @@ int nvfp4v_staircase(nvfp4v_ctx *ctx, int64_t n, int64_t k, int m_lo, int m_hi, 
                      int reps, size_t rotate_bytes, double *us_out);
 
 
+/* ---- StairCut: cutting a draft tree on the measured staircase ----------- */
+
+/* The cut rule of the pages' router (StairCut research page, "What it says":
+ * each round is priced on the measured verify-cost staircase and keeps the tree
+ * size that pays the most expected tokens per millisecond; release post: the
+ * candidate tree is cut to the node count with the most expected committed
+ * tokens per millisecond at the measured price, snapping to 7, 15, 23 or 31
+ * nodes). Host code; no GPU is touched.
+ *   us_by_rows  host double[max_rows]: us_by_rows[r - 1] is the measured time
+ *               in microseconds of a verify pass over r rows (the staircase).
+ *   parent      host int32[n_nodes]: the draft tree, nodes in an order where a
+ *               parent precedes its children; -1 = a child of the root (the
+ *               last committed token).
+ *   p_accept    host double[n_nodes] in [0, 1]: probability that the model's
+ *               own token at the node's position is the node's token, given
+ *               that its parent was accepted. Siblings are different tokens at
+ *               one position, so the probabilities of a node's children sum to
+ *               at most 1.
+ *   sizes       host int32[n_sizes] candidate node counts (NULL: 7, 15, 23,
+ *               31); a candidate above n_nodes means the whole tree.
+ * A cut to n nodes keeps the n nodes with the highest path probability P (the
+ * product of p along the root path; those nodes always form a subtree), is
+ * expected to commit E = 1 + sum of their P tokens (the accepted path plus the
+ * model's own token), and costs us_by_rows[n] (n + 1 rows: the kept nodes and
+ * the root). The candidate with the largest E / time wins; equal rates keep
+ * the smaller tree.
+ * Outputs: *n_keep, keep[n_nodes] (1 = kept), and if not NULL the winner's
+ * *expected_tokens and *tokens_per_ms.
+ * Errors: INVALID_ARG (null pointer, p outside [0, 1] or NaN, children's
+ * probabilities summing above 1, a price that is not positive and finite),
+ * SHAPE (n_nodes outside 1..NVFP4V_STAIRCUT_MAX_NODES, a parent that does not
+ * precede its child, a candidate < 1), M_RANGE (a candidate needs more rows
+ * than max_rows). */
+#define NVFP4V_STAIRCUT_MAX_NODES 4096
+int nvfp4v_staircut(const double *us_by_rows, int max_rows, const int32_t *parent,
+                    const double *p_accept, int n_nodes, const int32_t *sizes, int n_sizes,
+                    int32_t *n_keep, uint8_t *keep, double *expected_tokens,
+                    double *tokens_per_ms);
+
 /* ---- Full verify pass (chained layer stack) ----------------------------- */
 
 /* One layer of the dense stand-in stack. The pages give neither layer shapes
@@ -275,13 +314,23 @@ size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter, int
  *                           32 layers in which a producer wave per work-group
  *                           streams weights into LDS across GEMM boundaries
  *                           while its consumer waves compute (M <= 32; larger
- *                           M runs the chained launches).
+ *                           M runs the chained launches);
+ *   NVFP4V_PASS_STREAM      one cooperatively launched persistent kernel per
+ *                           32 layers, one work-group per CU, each with an
+ *                           equal rectangle of every GEMM: a weight wave
+ *                           streams tiles into a large LDS ring without ever
+ *                           waiting at a GEMM boundary, an activation wave
+ *                           loads each activation k-tile once and runs the
+ *                           grid barrier, and four consumer waves dequantise
+ *                           and multiply; split-K partials meet in one XCD's
+ *                           L2 (M <= 32; larger M runs the chained launches).
  * Each mode is deterministic (equal inputs give equal bits on every call); the
  * modes split K differently, so their fp32 sums can differ in the last bits.
  * Errors: INVALID_ARG. */
 #define NVFP4V_PASS_CHAIN 0
 #define NVFP4V_PASS_PERSISTENT 1
 #define NVFP4V_PASS_FLOW 2
+#define NVFP4V_PASS_STREAM 3
 int nvfp4v_set_pass_mode(nvfp4v_ctx *ctx, int mode);
 int nvfp4v_get_pass_mode(const nvfp4v_ctx *ctx);
 
@@ -315,6 +364,14 @@ int nvfp4v_verify_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers
 /* Synchronise the device and report whether the last persistent pass on this
  * context finished (NVFP4V_OK) or gave up at a barrier (NVFP4V_E_TIMEOUT). */
 int nvfp4v_pass_status(nvfp4v_ctx *ctx);
+/* Synchronise and return where the last persistent pass gave up: 0 if it did
+ * not, 1 at a grid barrier, 16..24 at one of the stream schedule's bounded
+ * waits (16: work-group places on the XCDs, 17: a free weight slot, 18: a free
+ * activation slot, 19: the consumers' end of a phase, 20: an activation
+ * k-tile, 21: a weight tile, 22: split-K partials, 23: the end of the last
+ * phase, 24: another wave gave up first). For diagnosis; nvfp4v_pass_status
+ * reports the failure itself. Errors: INVALID_ARG, HIP. */
+int nvfp4v_pass_error_site(nvfp4v_ctx *ctx);
 /* Work-groups of the last persistent pass launch (0 before the first). */
 int nvfp4v_last_pass_grid(const nvfp4v_ctx *ctx);
 /* Phase timeline of the last pass, for profiling (only when the context was

@@ -30,6 +30,7 @@ E_DISPATCH = -10
 PASS_CHAIN = 0
 PASS_PERSISTENT = 1
 PASS_FLOW = 2
+PASS_STREAM = 3
 MAX_M = 64
 
 _lib = None
@@ -81,6 +82,7 @@ def load():
     lib.nvfp4v_glue_sum.argtypes = [p, p, i64, p, i64, i64, i64, c.c_float, p, p]
     lib.nvfp4v_pass_workspace_bytes.argtypes = [i64, i64, i64, c.c_int]
     lib.nvfp4v_pass_status.argtypes = [p]
+    lib.nvfp4v_pass_error_site.argtypes = [p]
     lib.nvfp4v_last_pass_grid.argtypes = [p]
     lib.nvfp4v_set_pass_mode.argtypes = [p, c.c_int]
     lib.nvfp4v_get_pass_mode.argtypes = [p]
@@ -97,6 +99,7 @@ def load():
     lib.nvfp4v_fp8_pack_host.argtypes = [p, p, i64, i64, p]
     lib.nvfp4v_fp8_head_gemm.argtypes = [p, p, i64, i64, p, i64, p, p]
     lib.nvfp4v_fp8_head_gemm_pa.argtypes = [p, p, i64, i64, p, i64, p, p]
+    lib.nvfp4v_staircut.argtypes = [p, c.c_int, p, p, c.c_int, p, c.c_int, p, p, p, p]
     _lib = lib
     return lib
 
@@ -232,6 +235,33 @@ def fp8_pack_host(codes, row_scales):
     _check(load().nvfp4v_fp8_pack_host(_np_ptr(codes), _np_ptr(row_scales), n, k, _np_ptr(out)),
            "nvfp4v_fp8_pack_host")
     return out
+
+
+def staircut(us_by_rows, parent, p_accept, sizes=None):
+    """StairCut's cut of a draft tree on a measured staircase (host code).
+
+    us_by_rows[r - 1]: verify-pass microseconds at r rows; parent[v]: the
+    parent of node v (-1: the root), parents before children; p_accept[v]: the
+    probability that node v's token is accepted given its parent was; sizes:
+    candidate node counts (None: 7, 15, 23, 31). Returns (n_keep, keep mask
+    (uint8 per node), expected committed tokens, tokens per millisecond)."""
+    import numpy as np
+
+    us = np.ascontiguousarray(us_by_rows, dtype=np.float64)
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    p = np.ascontiguousarray(p_accept, dtype=np.float64)
+    if par.shape != p.shape or par.ndim != 1:
+        raise ValueError("parent and p_accept must be 1-D of one length")
+    sz = None if sizes is None else np.ascontiguousarray(sizes, dtype=np.int32)
+    keep = np.zeros(par.size, np.uint8)
+    n_keep = ctypes.c_int32()
+    e = ctypes.c_double()
+    rate = ctypes.c_double()
+    _check(load().nvfp4v_staircut(_np_ptr(us), us.size, _np_ptr(par), _np_ptr(p), par.size,
+                                  None if sz is None else _np_ptr(sz), 0 if sz is None else sz.size,
+                                  ctypes.byref(n_keep), _np_ptr(keep), ctypes.byref(e),
+                                  ctypes.byref(rate)), "nvfp4v_staircut")
+    return int(n_keep.value), keep, float(e.value), float(rate.value)
 
 
 class Context:
@@ -427,6 +457,10 @@ class Context:
     def pass_status(self) -> int:
         """Synchronise; NVFP4V_OK, or E_TIMEOUT if the last pass gave up at a barrier."""
         return int(load().nvfp4v_pass_status(self._h))
+
+    def pass_error_site(self) -> int:
+        """Synchronise; where the last persistent pass gave up (0: it did not)."""
+        return int(load().nvfp4v_pass_error_site(self._h))
 
     def set_pass_mode(self, mode: int) -> None:
         """PASS_CHAIN (four GEMM launches per layer), PASS_PERSISTENT or PASS_FLOW."""

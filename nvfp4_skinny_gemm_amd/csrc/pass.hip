@@ -542,6 +542,14 @@ extern "C" int nvfp4v_pass_status(nvfp4v_ctx *ctx) {
   return flag ? NVFP4V_E_TIMEOUT : NVFP4V_OK;
 }
 
+extern "C" int nvfp4v_pass_error_site(nvfp4v_ctx *ctx) {
+  if (!ctx) return NVFP4V_E_INVALID_ARG;
+  unsigned site = 0;
+  hipError_t e = hipMemcpy(&site, ctx->pass_sync + SYNC_ERROR, sizeof(unsigned), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_status(ctx, e);
+  return (int)site;
+}
+
 extern "C" int nvfp4v_verify_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers,
                                   int64_t hidden, int64_t inter, const uint16_t *h0, int64_t m,
                                   void *ws, size_t ws_bytes, uint16_t *h_out, uint16_t *trace,
@@ -583,6 +591,13 @@ extern "C" int nvfp4v_verify_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, i
     if (rc) return rc;
   }
   if (ctx->pass_mode == NVFP4V_PASS_CHAIN) return chain_pass(ctx, layers, n_layers, hidden, inter, h0, m, w, h_out, trace, stream);
+  if (ctx->pass_mode == NVFP4V_PASS_STREAM) {
+    // Rows beyond 32 keep the chained launches (two row blocks of activation
+    // fragments and accumulators per consumer wave is the most the stream
+    // kernel is built for).
+    if (m > 32) return chain_pass(ctx, layers, n_layers, hidden, inter, h0, m, w, h_out, trace, stream);
+    return stream_pass(ctx, layers, n_layers, hidden, inter, h0, m, w, h_out, trace, stream);
+  }
   if (ctx->pass_mode == NVFP4V_PASS_FLOW) {
     // Rows beyond 32 keep the chained launches (two row blocks of activation
     // fragments per consumer wave is the most the flow kernel is built for).

@@ -79,6 +79,14 @@ struct FlowShape {
   int nq_max;  // most work-groups any row block is spread over
 };
 
+// Work of one projection in stream mode (stream.hip): the grid's G
+// work-groups form G / gk row groups of R row tiles, each cut along K into gk
+// k-groups of S k-tiles; the gk work-groups of a row group run on one XCD.
+// unit = 2 when the row tiles come in (gate, up) pairs.
+struct StreamShape {
+  int gk, R, S, unit;
+};
+
 struct PassArgs {
   int n_layers;    // layers in this launch (<= LAYERS_PER_LAUNCH)
   int M;
@@ -86,6 +94,8 @@ struct PassArgs {
   int last_layer;  // index of the stack's last layer
   PhaseShape ph[4];
   FlowShape fs[4];
+  StreamShape ss[4];
+  int cus_per_xcd;  // stream mode: work-groups per XCD (the grid is 8 times that)
   const uint8_t *w[LAYERS_PER_LAUNCH][4];
   float ts[LAYERS_PER_LAUNCH][4];
   float cst[4];  // glue constants: H^-1/2, H^-1/2, (2H)^-1/2, I^-1/2
@@ -144,9 +154,12 @@ __device__ inline bool barrier_wait(unsigned *sync, unsigned gen) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   while (__hip_atomic_load(&sync[SYNC_RELEASE], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < gen) {
     __builtin_amdgcn_s_sleep(1);
-    if (__hip_atomic_load(&sync[SYNC_ERROR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0 ||
-        __builtin_amdgcn_s_memrealtime() - t0 > BARRIER_TIMEOUT_TICKS) {
-      __hip_atomic_store(&sync[SYNC_ERROR], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (__hip_atomic_load(&sync[SYNC_ERROR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0) return false;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > BARRIER_TIMEOUT_TICKS) {
+      // The error word keeps the first site that gave up (1: a grid barrier).
+      unsigned zero = 0;
+      (void)__hip_atomic_compare_exchange_strong(&sync[SYNC_ERROR], &zero, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_SYSTEM);
       return false;
     }
   }
@@ -190,6 +203,11 @@ __device__ inline GemmArgs phase_gemm(const PassArgs &a, int p) {
   }
   return g;
 }
+
+// The pass in stream mode (stream.hip): one cooperative launch per 32 layers.
+int stream_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_t H, int64_t I,
+                const uint16_t *h0, int64_t m, const PassWs &w, uint16_t *h_out, uint16_t *trace,
+                hipStream_t stream);
 
 // The pass in flow mode (flow.hip): one cooperative launch per 32 layers.
 int flow_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_t H, int64_t I,

@@ -141,3 +141,44 @@ def fp8_codes(n: int, k: int, seed: int = 0, stream: str = "fp8") -> np.ndarray:
 def fp8_row_scales(n: int, seed: int = 0, stream: str = "fp8s") -> np.ndarray:
     """fp32 row scales [n] spread over 2^-14 .. 2^-6 (|w| / 448 for weights of a few 1e-3 to 1e-1)."""
     return np.exp2(rng(seed, stream, n).uniform(-14.0, -6.0, size=n)).astype(np.float32)
+
+
+def draft_tree(n: int, seed: int = 0, stream: str = "tree", shape: str = "random"):
+    """A synthetic draft tree of n nodes for StairCut's cut: (parent int32[n],
+    p_accept float64[n]). Parents come before their children (-1 = the root).
+    shape "random": each node hangs under the root or an earlier node, chosen
+    uniformly; "chain": node v under v - 1; "wide": under the root or one of
+    the first three nodes. Each node's children share an acceptance mass
+    m ~ U(0.3, 0.98) split by uniform weights, so the probabilities of siblings
+    sum to m <= 1 (siblings are different tokens at one position)."""
+    g = rng(seed, stream, n)
+    if shape == "chain":
+        parent = np.arange(-1, n - 1, dtype=np.int32)
+    elif shape == "wide":
+        parent = np.array([-1] + [int(g.integers(-1, min(v, 3))) for v in range(1, n)], np.int32)
+    else:
+        parent = np.array([int(g.integers(-1, v)) for v in range(n)], np.int32)
+    p = np.zeros(n, np.float64)
+    for u in range(-1, n):
+        kids = np.nonzero(parent == u)[0]
+        if kids.size == 0:
+            continue
+        mass = g.uniform(0.3, 0.98)
+        w = g.uniform(0.05, 1.0, kids.size)
+        p[kids] = mass * w / w.sum()
+    return parent, p
+
+
+def staircase_us(max_rows: int = 64, seed: int = 0, stream: str = "stairs", base: float = 3800.0,
+                 step_rows: int = 8, step: float = 0.2):
+    """A synthetic staircase for the cut: us_by_rows[r - 1], flat within each
+    block of step_rows rows with a jump of up to `step` (relative, uniform) at
+    every block boundary and small seeded noise; for CPU tests of the cut."""
+    g = rng(seed, stream, max_rows, step_rows)
+    us = np.empty(max_rows, np.float64)
+    level = base
+    for r in range(1, max_rows + 1):
+        if r > 1 and (r - 1) % step_rows == 0:
+            level *= 1.0 + g.uniform(0.0, step)
+        us[r - 1] = level * (1.0 + g.uniform(-0.01, 0.01))
+    return us

@@ -124,6 +124,16 @@ def test_head_argument_errors(torch_cuda, ctx):
     with pytest.raises(nv.Nvfp4vError) as e:
         ctx.fp8_head_gemm(a, packed, 32, 256)
     assert e.value.status == nv.E_M_RANGE
+    # a K that is not a multiple of 16 is the library's shape error
+    a200 = torch.zeros((4, 200), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(nv.Nvfp4vError) as e:
-        ctx.fp8_head_gemm(a[:4], packed, 32, 200)
+        ctx.fp8_head_gemm(a200, packed, 32, 200)
     assert e.value.status == nv.E_SHAPE
+    # a tensor that does not match the sizes passed is refused by the binding
+    # before its address reaches the library
+    with pytest.raises(ValueError):
+        ctx.fp8_head_gemm(a[:4], packed, 32, 200)
+    with pytest.raises(ValueError):
+        ctx.verify_gemm(a[:4], packed, 32, 128)
+    with pytest.raises(ValueError):
+        ctx.fp8_head_gemm(a[:4], packed[:100], 32, 256)

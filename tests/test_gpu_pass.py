@@ -96,9 +96,11 @@ def manual_chain(torch, ctx, packed, h0, H, I):
 
 
 MODES = [pytest.param(nv.PASS_CHAIN, id="chain"), pytest.param(nv.PASS_PERSISTENT, id="persistent")]
-# The flow schedule cuts K at other points than single calls do, so it is
-# checked against the oracle (and for determinism), not bitwise against them.
-ALL_MODES = MODES + [pytest.param(nv.PASS_FLOW, id="flow")]
+# The flow and stream schedules cut K at other points than single calls do, so
+# they are checked against the oracle (and for determinism), not bitwise
+# against them.
+CUT_MODES = [pytest.param(nv.PASS_FLOW, id="flow"), pytest.param(nv.PASS_STREAM, id="stream")]
+ALL_MODES = MODES + CUT_MODES
 
 
 @pytest.fixture
@@ -183,15 +185,18 @@ def test_graph_replays_equal_eager(torch_cuda, mode_ctx):
     packed, arr = small_stack(torch, ctx, L, H, I, seed=1)
     h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=4).view(np.int16)).cuda().view(torch.bfloat16)
     ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
-    eager = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    eager = torch.zeros((m, H), dtype=torch.bfloat16, device="cuda")
     ctx.verify_pass(arr, H, I, h0[:m], ws, eager)
     torch.cuda.synchronize()
+    assert ctx.pass_status() == nv.OK, "eager pass gave up at site %d" % ctx.pass_error_site()
+    assert torch.isfinite(eager.float()).all() and eager.float().abs().sum() > 0
     out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         ctx.verify_pass(arr, H, I, h0[:m], ws, out)
     torch.cuda.current_stream().wait_stream(s)
+    assert ctx.pass_status() == nv.OK, "side-stream pass gave up at site %d" % ctx.pass_error_site()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         ctx.verify_pass(arr, H, I, h0[:m], ws, out)
@@ -199,6 +204,7 @@ def test_graph_replays_equal_eager(torch_cuda, mode_ctx):
         out.zero_()
         g.replay()
         torch.cuda.synchronize()
+        assert ctx.pass_status() == nv.OK, "replay %d gave up at site %d" % (rep, ctx.pass_error_site())
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), "replay %d" % rep
         # unrelated eager work between replays
         ctx.verify_gemm(h0[:m], packed[0]["qkv"], 3 * H, H)
@@ -308,7 +314,7 @@ def run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed, sample):
     h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
     trace = torch.empty((L, m, H), dtype=torch.bfloat16, device="cuda")
     ctx.verify_pass(arr, H, I, h0[:m], ws, h_out, trace=trace)
-    assert ctx.pass_status() == nv.OK
+    assert ctx.pass_status() == nv.OK, "pass gave up at site %d" % ctx.pass_error_site()
     torch.cuda.synchronize()
     assert torch.isfinite(trace.float()).all(), "non-finite activations in the pass"
     C, acts = workspace_views(ws.cpu().numpy(), m, H, I, L)
@@ -352,25 +358,24 @@ def run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed, sample):
     return trace
 
 
-@pytest.mark.parametrize("shape", [(256, 512, 3), (2048, 8192, 2), (1040, 2064, 2)],
-                         ids=["tiny", "split-pieces", "ragged"])
+@pytest.mark.parametrize("mode_ctx", CUT_MODES, indirect=True)
+@pytest.mark.parametrize("shape", [(256, 512, 3), (2048, 8192, 2), (1040, 2064, 2), (3072, 5120, 2)],
+                         ids=["tiny", "split-pieces", "ragged", "leftover-units"])
 @pytest.mark.parametrize("m", [1, 8, 16, 17, 32])
-def test_flow_pass_against_oracle(torch_cuda, ctx, oracle_mod, shape, m):
-    """Flow schedule: the last layer's GEMMs (every row) against the oracle and
-    its glue bitwise. "tiny" leaves most work-groups without work, "split-pieces"
-    spreads row blocks over several work-groups (partial sums in k order),
-    "ragged" has row tiles and k-tiles that do not fill a row block or a
-    k-tile. The same pass again is bitwise identical."""
-    torch = torch_cuda
+def test_cut_pass_against_oracle(torch_cuda, mode_ctx, oracle_mod, shape, m):
+    """Flow and stream schedules: the last layer's GEMMs (every row) against the
+    oracle and its glue bitwise. "tiny" leaves most work-groups without work,
+    "split-pieces" spreads row blocks over several work-groups (partial sums in
+    k order), "ragged" has row tiles and k-tiles that do not fill a row block
+    or a k-tile, "leftover-units" gives the stream schedule row groups whose
+    row count is not a multiple of four units. The same pass again is bitwise
+    identical."""
+    torch, ctx = torch_cuda, mode_ctx
     H, I, L = shape
-    ctx.set_pass_mode(nv.PASS_FLOW)
-    try:
-        log("flow pass H=%d I=%d L=%d M=%d" % (H, I, L, m))
-        t1 = run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed=4, sample=None)
-        t2 = run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed=4, sample=64)
-        assert torch.equal(t1.view(torch.int16), t2.view(torch.int16)), "flow pass not deterministic"
-    finally:
-        ctx.set_pass_mode(nv.PASS_CHAIN)
+    log("pass mode %d H=%d I=%d L=%d M=%d" % (ctx.get_pass_mode(), H, I, L, m))
+    t1 = run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed=4, sample=None)
+    t2 = run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed=4, sample=64)
+    assert torch.equal(t1.view(torch.int16), t2.view(torch.int16)), "pass not deterministic"
 
 
 @pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
@@ -383,36 +388,31 @@ def test_ragged_k_pass_against_oracle(torch_cuda, mode_ctx, oracle_mod):
         run_and_check_last_layer(torch, ctx, oracle_mod, m, 1040, 2064, 2, seed=6, sample=None)
 
 
+@pytest.mark.parametrize("mode_ctx", CUT_MODES, indirect=True)
 @pytest.mark.parametrize("m", [16, 32])
-def test_flow_pass_longer_than_one_launch(torch_cuda, ctx, oracle_mod, m):
-    """40 layers: two flow launches (32 + 8 layers); the last layer is checked
-    against the oracle and the whole trace is deterministic."""
-    torch = torch_cuda
-    ctx.set_pass_mode(nv.PASS_FLOW)
-    try:
-        t1 = run_and_check_last_layer(torch, ctx, oracle_mod, m, 256, 512, 40, seed=9, sample=None)
-        t2 = run_and_check_last_layer(torch, ctx, oracle_mod, m, 256, 512, 40, seed=9, sample=None)
-        assert torch.equal(t1.view(torch.int16), t2.view(torch.int16))
-        assert torch.isfinite(t1.float()).all()
-    finally:
-        ctx.set_pass_mode(nv.PASS_CHAIN)
+def test_cut_pass_longer_than_one_launch(torch_cuda, mode_ctx, oracle_mod, m):
+    """40 layers: two persistent launches (32 + 8 layers); the last layer is
+    checked against the oracle and the whole trace is deterministic."""
+    torch, ctx = torch_cuda, mode_ctx
+    t1 = run_and_check_last_layer(torch, ctx, oracle_mod, m, 256, 512, 40, seed=9, sample=None)
+    t2 = run_and_check_last_layer(torch, ctx, oracle_mod, m, 256, 512, 40, seed=9, sample=None)
+    assert torch.equal(t1.view(torch.int16), t2.view(torch.int16))
+    assert torch.isfinite(t1.float()).all()
 
 
-def test_flow_pass_large_m_falls_back(torch_cuda, ctx):
-    """M > 32 in flow mode runs the chained launches: bitwise the composition."""
-    torch = torch_cuda
+@pytest.mark.parametrize("mode_ctx", CUT_MODES, indirect=True)
+def test_cut_pass_large_m_falls_back(torch_cuda, mode_ctx):
+    """M > 32 in the flow and stream modes runs the chained launches: bitwise
+    the composition."""
+    torch, ctx = torch_cuda, mode_ctx
     H, I, L, m = 256, 512, 2, 40
-    ctx.set_pass_mode(nv.PASS_FLOW)
-    try:
-        packed, arr = small_stack(torch, ctx, L, H, I)
-        h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=3).view(np.int16)).cuda().view(torch.bfloat16)
-        ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
-        h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
-        ctx.verify_pass(arr, H, I, h0[:m], ws, h_out)
-        ref = manual_chain(torch, ctx, packed, h0[:m], H, I)
-        assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16))
-    finally:
-        ctx.set_pass_mode(nv.PASS_CHAIN)
+    packed, arr = small_stack(torch, ctx, L, H, I)
+    h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=3).view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
+    h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    ctx.verify_pass(arr, H, I, h0[:m], ws, h_out)
+    ref = manual_chain(torch, ctx, packed, h0[:m], H, I)
+    assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16))
 
 
 @pytest.mark.parametrize("mode_ctx", ALL_MODES, indirect=True)
