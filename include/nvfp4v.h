@@ -6,7 +6,9 @@
  * so the pass is a skinny GEMM that streams 4-bit weights from HBM and whose
  * cost is flat in the row count until a tile boundary is crossed
  * (TandemLLM manual, "What TandemLLM is", 1.2 "Two levers"; StairCut research
- * page, "What it says"). This library computes, for M = 1..64 rows,
+ * page, "What it says"). This library computes, for M = 1..128 rows (up to
+ * four sequences' trees of 32 rows checked in one pass: TandemLLM manual, 1.4
+ * "What runs today", requests decoding together share one verify pass),
  *
  *     C[M, N] (fp32) = ts * A[M, K] (bf16) * W[N, K]^T,
  *     W[j, k] = E2M1(code[j, k]) * E4M3(scale[j, k / 16])
@@ -66,8 +68,9 @@ extern "C" {
 #define NVFP4V_E_WORKSPACE (-8)   /* the request exceeds the context workspace */
 #define NVFP4V_E_TIMEOUT (-9)     /* a persistent pass gave up at a grid barrier */
 #define NVFP4V_E_DISPATCH (-10)   /* split-K pieces of a row block ran on two XCDs */
+#define NVFP4V_E_TABLE (-11)      /* a tile-table file is unreadable or malformed  */
 
-#define NVFP4V_MAX_M 64
+#define NVFP4V_MAX_M 128
 
 typedef struct nvfp4v_ctx nvfp4v_ctx;
 
@@ -75,14 +78,38 @@ typedef struct nvfp4v_ctx nvfp4v_ctx;
  * properties, the tile table, and a split-K workspace (partial sums and
  * arrival counters) allocated here once, so that nvfp4v_verify_gemm never
  * allocates and can be captured in a HIP graph. The caller destroys it.
+ * tile_table_path: NULL for the built-in gfx950 table (the library's
+ * tables/gfx950.txt, compiled in), else a table file in that format, whose
+ * rules are tried before the built-in ones (see nvfp4v_load_tile_table;
+ * TandemLLM manual, "What TandemLLM is", 1.1 "The test environment": the
+ * kernels' tile tables come from the board they run on).
  * Create also runs a short synchronous dispatch probe: when the device deals
  * the work-groups of a launch out to its XCDs round-robin by linear id (as
  * gfx950 does in its one-partition mode), split-K GEMMs exchange their
  * partial sums through the L2 of the one XCD that runs a row block's pieces;
  * otherwise, or with NVFP4V_SPLITK_EXCHANGE=memory in the environment,
  * through memory. Both give bitwise identical C. */
-int nvfp4v_create(nvfp4v_ctx **out, int device);
+int nvfp4v_create(nvfp4v_ctx **out, int device, const char *tile_table_path);
 void nvfp4v_destroy(nvfp4v_ctx *ctx);
+
+/* (Re)load the context's tile table from a text file; NULL returns it to the
+ * built-in table alone. Format: lines of whitespace-separated fields, '#'
+ * starts a comment; one "arch gfx950" line (the only arch this library is built
+ * for), then rules
+ *     rule <nrt_lo> <nrt_hi> <nkt_lo> <nkt_hi> <m_lo> <m_hi> <kernel> <R> <ksplit>
+ * (at most 64): a GEMM of nrt row tiles (16 weight rows each) and nkt k-tiles
+ * (256 elements of K each) at M rows takes the plan of the first rule whose
+ * inclusive ranges hold all three ("*" is an open end); kernel "reg" (waves
+ * split K, R row tiles per work-group: 1, 2, 4 or 8) or "lds" (activations
+ * staged in LDS, waves split N, R row tiles per wave: 1, or 2 up to 32 rows);
+ * ksplit work-groups along K (1..64), summed in a fixed order. GEMMs that no
+ * rule holds take the built-in table. Host only (no HIP call); the loaded rules
+ * apply to the context's later calls. NVFP4V_PLAN=r=<R>,ks=<S> (or
+ * n:r=<R>,ks=<S> for the LDS variant) in the environment still overrides both.
+ * Errors: INVALID_ARG, TABLE (unreadable file, unknown field, wrong arch, a
+ * range, R or ksplit out of bounds, a kernel not built for some M of its
+ * range, more than 64 rules); on error the previous table stays. */
+int nvfp4v_load_tile_table(nvfp4v_ctx *ctx, const char *path);
 
 /* Synchronise the device, then report the device-side errors that GEMMs on
  * this context recorded since it was created or last reported one:
@@ -149,9 +176,10 @@ int nvfp4v_unpack(nvfp4v_ctx *ctx, const void *packed_dev, int64_t n, int64_t k,
  *              aligned, K % 8 == 0 for that alignment to hold per row
  *   packed_dev nvfp4v_pack output for the N x K weights, 16-byte aligned
  *   c_dev      fp32, row-major [M][N], 16-byte aligned; fully overwritten
- * M in 1..64. Does not allocate; safe to capture in a HIP graph. Two kernels
- * run: A is packed into the context's buffer (K up to 131072 at M = 64,
- * else WORKSPACE), then the GEMM.
+ * M in 1..128. Does not allocate; safe to capture in a HIP graph. Two kernels
+ * run per block of 64 rows: the block of A is packed into the context's
+ * buffer (K up to 131072, else WORKSPACE), then the GEMM over it (rows are
+ * independent, so M > 64 reads the weights once per block).
  * Errors: INVALID_ARG, SHAPE, M_RANGE, ALIGN, WORKSPACE, HIP, FAULT. */
 int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_t k,
                        const void *packed_dev, int64_t n, float ts, float *c_dev,
@@ -160,7 +188,9 @@ int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_
 /* Activations pre-packed in the GEMM's MFMA fragment order, for callers that
  * produce the next GEMM's input themselves (the chained pass writes them from
  * its glue kernels). nvfp4v_verify_gemm does this packing internally, into the
- * context's buffer, before each call.
+ * context's buffer, before each call. More than 64 rows are packed as
+ * consecutive blocks of 64 rows (the last one shorter), each in the layout of
+ * its own row count.
  *   nvfp4v_act_packed_bytes: bytes of the packed form of A[M][K] (0 if bad).
  *   nvfp4v_pack_activations: a_dev bf16 [M][K] row-major -> act_dev (16-byte
  *     aligned, nvfp4v_act_packed_bytes bytes). Errors: INVALID_ARG, M_RANGE,
@@ -192,9 +222,9 @@ int nvfp4v_verify_gemm_pa(nvfp4v_ctx *ctx, const void *act_dev, int64_t m, int64
  *   nvfp4v_fp8_head_gemm: C[M][N] fp32 = A[M][K] * (s . W8)^T for bf16 A
  *     (device, row-major, 16-byte aligned), the packed head (device, 16-byte
  *     aligned), C (device, row-major, 16-byte aligned, fully overwritten).
- *     M in 1..32. A is packed into the context's buffer first (two kernels).
- *     Does not allocate. Errors: INVALID_ARG, M_RANGE, SHAPE, ALIGN, WORKSPACE,
- *     HIP, FAULT.
+ *     M in 1..128, one launch per block of 64 rows (each block of A is packed
+ *     into the context's buffer first). Does not allocate. Errors:
+ *     INVALID_ARG, M_RANGE, SHAPE, ALIGN, WORKSPACE, HIP, FAULT.
  *   nvfp4v_fp8_head_gemm_pa: the same with A given packed
  *     (nvfp4v_pack_activations). */
 size_t nvfp4v_fp8_packed_bytes(int64_t n, int64_t k);

@@ -27,11 +27,12 @@ E_NONFINITE = -7
 E_WORKSPACE = -8
 E_TIMEOUT = -9
 E_DISPATCH = -10
+E_TABLE = -11
 PASS_CHAIN = 0
 PASS_PERSISTENT = 1
 PASS_FLOW = 2
 PASS_STREAM = 3
-MAX_M = 64
+MAX_M = 128
 
 _lib = None
 
@@ -54,7 +55,8 @@ def load():
     c = ctypes
     p = c.c_void_p
     i64 = c.c_int64
-    lib.nvfp4v_create.argtypes = [c.POINTER(p), c.c_int]
+    lib.nvfp4v_create.argtypes = [c.POINTER(p), c.c_int, c.c_char_p]
+    lib.nvfp4v_load_tile_table.argtypes = [p, c.c_char_p]
     lib.nvfp4v_destroy.argtypes = [p]
     lib.nvfp4v_destroy.restype = None
     lib.nvfp4v_strerror.argtypes = [c.c_int]
@@ -267,12 +269,19 @@ def staircut(us_by_rows, parent, p_accept, sizes=None):
 class Context:
     """An nvfp4v context on one GPU (owns the split-K workspace)."""
 
-    def __init__(self, device: int = 0):
+    def __init__(self, device: int = 0, tile_table: str = None):
+        """tile_table: a tile-table file (None: the built-in gfx950 table)."""
         lib = load()
         h = ctypes.c_void_p()
-        _check(lib.nvfp4v_create(ctypes.byref(h), int(device)), "nvfp4v_create")
+        path = None if tile_table is None else os.fsencode(tile_table)
+        _check(lib.nvfp4v_create(ctypes.byref(h), int(device), path), "nvfp4v_create")
         self._h = h
         self.device = device
+
+    def load_tile_table(self, path: str = None) -> None:
+        """Load a tile-table file (None: back to the built-in table alone)."""
+        _check(load().nvfp4v_load_tile_table(self._h, None if path is None else os.fsencode(path)),
+               "nvfp4v_load_tile_table")
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:

@@ -31,15 +31,31 @@ CFLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, "-I", OBJ, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
+TABLE = os.path.join(HERE, "tables", "gfx950.txt")
+
+
+def _embed_table() -> None:
+    """The built-in tile table is tables/gfx950.txt, compiled into the library
+    as a string (the file stays the one source of its rows)."""
+    text = open(TABLE).read()
+    assert ")TABLE\"" not in text
+    out = os.path.join(OBJ, "tile_table_gfx950.inc")
+    body = 'R"TABLE(' + text + ')TABLE"\n'
+    if not os.path.exists(out) or open(out).read() != body:
+        with open(out, "w") as f:
+            f.write(body)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
+    _embed_table()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

@@ -33,12 +33,19 @@ static constexpr size_t kCounters = 4096;
 // K = 131072 (larger requests return NVFP4V_E_WORKSPACE).
 static constexpr size_t kActBytes = size_t(16) << 20;
 
-extern "C" int nvfp4v_create(nvfp4v_ctx **out, int device) {
+extern "C" int nvfp4v_create(nvfp4v_ctx **out, int device, const char *tile_table_path) {
   if (!out || device < 0) return NVFP4V_E_INVALID_ARG;
   *out = nullptr;
   if (fault_injected()) return NVFP4V_E_FAULT;
   nvfp4v_ctx *ctx = new (std::nothrow) nvfp4v_ctx();
   if (!ctx) return NVFP4V_E_INVALID_ARG;
+  if (tile_table_path) {
+    const int rc = nvfp4v_load_tile_table(ctx, tile_table_path);
+    if (rc) {
+      delete ctx;
+      return rc;
+    }
+  }
   ctx->device = device;
   hipError_t e = hipSetDevice(device);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&ctx->num_cus, hipDeviceAttributeMultiprocessorCount, device);
@@ -142,7 +149,7 @@ extern "C" const char *nvfp4v_strerror(int status) {
     case NVFP4V_OK: return "ok";
     case NVFP4V_E_INVALID_ARG: return "invalid argument (null pointer or context)";
     case NVFP4V_E_SHAPE: return "bad shape (need N >= 1, K >= 16, K % 16 == 0)";
-    case NVFP4V_E_M_RANGE: return "M out of range (1..64)";
+    case NVFP4V_E_M_RANGE: return "M out of range";
     case NVFP4V_E_ALIGN: return "device pointer not 16-byte aligned";
     case NVFP4V_E_HIP: return "HIP runtime or launch error";
     case NVFP4V_E_FAULT: return "injected fault (NVFP4V_FAULT=launch)";
@@ -150,6 +157,7 @@ extern "C" const char *nvfp4v_strerror(int status) {
     case NVFP4V_E_WORKSPACE: return "request exceeds the context's split-K workspace";
     case NVFP4V_E_TIMEOUT: return "a persistent pass timed out at a grid barrier";
     case NVFP4V_E_DISPATCH: return "the pieces of a split-K row block ran on different XCDs (outputs undefined)";
+    case NVFP4V_E_TABLE: return "tile table unreadable or malformed (or for another arch)";
     default: return "unknown status";
   }
 }

@@ -633,6 +633,7 @@ int flow_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_t
   }
   a.h_out = h_out;
   a.trace = trace;
+  a.trace_m = (int)w.trace_m;
   a.part = ctx->partials;
   a.counters = ctx->counters;
   a.sync = ctx->pass_sync;

@@ -42,9 +42,11 @@
 //    exchanges agree bitwise (TandemLLM manual, 1.7 "The paper": the 4-bit
 //    kernels keep a fixed reduction order). No float atomics.
 #include <algorithm>
+#include <cctype>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <string>
 #include <vector>
 
 #include "gemm_device.h"
@@ -162,28 +164,104 @@ __global__ void k_pack_act(const uint16_t *__restrict__ A, int M, int K, int mbl
 
 namespace nvfp4v {
 
-// Tile table for gfx950. R = row tiles per wave item sharing one activation
-// fragment, ksplit = work-groups along K, "LDS" = the variant whose waves
-// split N and share activations staged in LDS. From sweeps of R in {1,2,4,8}
-// x ksplit in {1,2,3,4,6,8} x both variants, one projection at a time, inside
-// the graph-replayed 64-layer pass (the other projections at their chosen
-// plans), at M = 1, 8, 9, 16, 17, 24, 32, and of single launches over 1 GiB
-// of rotated weight copies for the LM head and M > 32:
-//  * up to 8 rows: R = 2 everywhere, K split 3 for the K-heavy narrow down
-//    projection [5120 x 17408];
-//  * 9..16 rows (twice the activation bytes per k-tile): R = 4 for q|k|v (960
-//    row tiles), LDS with K split 3 from 1024 row tiles (gate|up: 2176 in the
-//    pass, 1088 for one of the pair alone, 15 % faster than R = 4 there), LDS
-//    with K split 6 for down, R = 2 for o;
-//  * 17..32 rows: R = 4 with K split 3 for down, R = 4 for q|k|v and gate|up,
-//    R = 2 for o;
-//  * the 151936-row LM head: LDS with R = 2 per wave up to 32 rows;
-//  * beyond 32 rows: R = 4 with K split 3 for down, and for the narrow
-//    square matrices beyond 48 rows; R = 2 for those up to 48 rows; R = 4
-//    for the wide ones.
-// Split-K exchanges meet in one XCD's L2 (unit_tail), which is what makes the
-// K splits at 9..16 rows pay.
-// NVFP4V_PLAN="r=<R>,ks=<ksplit>" overrides both (used by tuning sweeps).
+// ---------------------------------------------------------------------------
+// Tile table. The built-in table is the library's tables/gfx950.txt, compiled
+// in (the build embeds the file); a context may load another file, whose rules
+// are tried first. The rows were measured on MI355X (see the file's header).
+// ---------------------------------------------------------------------------
+static const char kBuiltinTable[] =
+#include "tile_table_gfx950.inc"
+    ;
+
+// A field of a rule: a non-negative integer, or "*" (returns `open`).
+static bool parse_bound(const char *tok, int open, int *out) {
+  if (std::strcmp(tok, "*") == 0) {
+    *out = open;
+    return true;
+  }
+  char *end = nullptr;
+  const long v = std::strtol(tok, &end, 10);
+  if (!end || *end != 0 || v < 0 || v > (1L << 30)) return false;
+  *out = (int)v;
+  return true;
+}
+
+// Every M of the rule's range has a compiled kernel for its kernel and R.
+static bool rule_has_kernels(const TileRule &t) {
+  for (int mb = (t.m_lo + 15) / 16; mb <= (t.m_hi + 15) / 16; ++mb) {
+    if (t.lds ? !pick_lds_kernel(mb, t.r) : !ring_depth(mb, t.r, 4)) return false;
+  }
+  return true;
+}
+
+int parse_tile_table(const char *text, TileRule *rules, int *n_rules) {
+  int n = 0;
+  bool arch_ok = false;
+  const char *p = text;
+  while (*p) {
+    const char *eol = std::strchr(p, '\n');
+    const size_t len = eol ? (size_t)(eol - p) : std::strlen(p);
+    std::string line(p, len);
+    p = eol ? eol + 1 : p + len;
+    const size_t hash = line.find('#');
+    if (hash != std::string::npos) line.resize(hash);
+    std::vector<std::string> tok;
+    size_t i = 0;
+    while (i < line.size()) {
+      while (i < line.size() && std::isspace((unsigned char)line[i])) ++i;
+      size_t j = i;
+      while (j < line.size() && !std::isspace((unsigned char)line[j])) ++j;
+      if (j > i) tok.emplace_back(line.substr(i, j - i));
+      i = j;
+    }
+    if (tok.empty()) continue;
+    if (tok[0] == "arch") {
+      if (tok.size() != 2 || tok[1] != "gfx950") return NVFP4V_E_TABLE;
+      arch_ok = true;
+      continue;
+    }
+    if (tok[0] != "rule" || tok.size() != 10 || n >= MAX_TILE_RULES) return NVFP4V_E_TABLE;
+    TileRule t;
+    if (!parse_bound(tok[1].c_str(), 1, &t.nrt_lo) || !parse_bound(tok[2].c_str(), 1 << 30, &t.nrt_hi) ||
+        !parse_bound(tok[3].c_str(), 1, &t.nkt_lo) || !parse_bound(tok[4].c_str(), 1 << 30, &t.nkt_hi) ||
+        !parse_bound(tok[5].c_str(), 1, &t.m_lo) || !parse_bound(tok[6].c_str(), CHUNK_M, &t.m_hi))
+      return NVFP4V_E_TABLE;
+    if (tok[7] == "lds") t.lds = 1;
+    else if (tok[7] == "reg") t.lds = 0;
+    else return NVFP4V_E_TABLE;
+    if (!parse_bound(tok[8].c_str(), 0, &t.r) || !parse_bound(tok[9].c_str(), 0, &t.ksplit)) return NVFP4V_E_TABLE;
+    if (t.nrt_lo < 1 || t.nrt_lo > t.nrt_hi || t.nkt_lo < 1 || t.nkt_lo > t.nkt_hi || t.m_lo < 1 ||
+        t.m_lo > t.m_hi || t.m_hi > CHUNK_M || t.ksplit < 1 || t.ksplit > 64 || !rule_has_kernels(t))
+      return NVFP4V_E_TABLE;
+    rules[n++] = t;
+  }
+  if (!arch_ok) return NVFP4V_E_TABLE;
+  *n_rules = n;
+  return NVFP4V_OK;
+}
+
+static const TileRule *find_rule(const TileRule *rules, int n, int64_t nrt, int64_t nkt, int64_t m) {
+  for (int i = 0; i < n; ++i) {
+    const TileRule &t = rules[i];
+    if (nrt >= t.nrt_lo && nrt <= t.nrt_hi && nkt >= t.nkt_lo && nkt <= t.nkt_hi && m >= t.m_lo && m <= t.m_hi)
+      return &t;
+  }
+  return nullptr;
+}
+
+static const TileRule *builtin_rules(int *n) {
+  static TileRule rules[MAX_TILE_RULES];
+  static int count = -1;
+  if (count < 0) {
+    int c = 0;
+    count = parse_tile_table(kBuiltinTable, rules, &c) == NVFP4V_OK ? c : 0;
+  }
+  *n = count;
+  return rules;
+}
+
+// NVFP4V_PLAN="r=<R>,ks=<ksplit>" (or "n:..." for the LDS variant) overrides
+// the table (used by tuning sweeps).
 static void finish_grid(const nvfp4v_ctx *ctx, Plan *p) {
   p->nrb = p->grid_x;
   p->xcd_local = p->ksplit > 1 && ctx && ctx->xcd_local;
@@ -195,28 +273,21 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
   p->waves = WG_WAVES;
   const int64_t nrt = L.nrt;
   const int nkt = (int)L.nkt;
-  const bool narrow = nrt <= 640, deep = nkt >= 48;  // o and down vs q|k|v and gate|up
   int want_ks = 1;
-  p->lds = 0;
   int want_d = 2;
-  if (p->mblocks == 1) {
-    p->rb = nrt >= 4096 && m > 1 ? 4 : 2;
-    if (deep && narrow) {
-      want_ks = 3;
-      if (m > 8) p->lds = 1, p->rb = 1, want_ks = 6;
-    } else if (m > 8 && !narrow && nrt < 4096) {
-      if (nrt >= 1024) p->lds = 1, p->rb = 1, want_ks = 3;
-      else p->rb = 4;
-    }
-  } else if (p->mblocks == 2) {
-    p->rb = nrt >= 4096 ? 8 : narrow && !deep ? 2 : 4;
-    if (deep && narrow) want_ks = 3;
-  } else {
-    p->rb = nrt >= 640 || deep || p->mblocks == 4 ? 4 : 2;
-    if (narrow && (deep || p->mblocks == 4)) want_ks = 3;
+  p->lds = 0;
+  p->rb = 2;
+  const TileRule *rule = ctx && ctx->n_rules > 0 ? find_rule(ctx->rules, ctx->n_rules, nrt, nkt, m) : nullptr;
+  if (!rule) {
+    int nb = 0;
+    const TileRule *b = builtin_rules(&nb);
+    rule = find_rule(b, nb, nrt, nkt, m);
   }
-  // The LM head up to 32 rows: activations staged in LDS, R = 2 per wave.
-  if (p->mblocks <= 2 && nrt >= 4096) p->lds = 1, p->rb = 2, want_ks = 1;
+  if (rule) {
+    p->lds = rule->lds;
+    p->rb = rule->r;
+    want_ks = rule->ksplit;
+  }
   if (const char *ov = std::getenv("NVFP4V_PLAN")) {
     int r = 0, k2 = 0;
     if (std::sscanf(ov, "n:r=%d,ks=%d", &r, &k2) == 2 && pick_lds_kernel(p->mblocks, r)) {
@@ -231,13 +302,13 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
       if (std::sscanf(ov, "r=%*d,ks=%*d,d=%d", &d2) == 1 && d2 >= 1) want_d = d2;
     }
   }
-  int force_ks = want_ks;
+  if (p->lds && !pick_lds_kernel(p->mblocks, p->rb)) p->lds = 0, p->rb = 2;
   if (!p->lds && !ring_depth(p->mblocks, p->rb, 4)) p->rb = 4;
   p->depth = p->lds ? 0 : ring_depth(p->mblocks, p->rb, want_d);
   const int64_t rows_per_group = p->lds ? (int64_t)WG_WAVES * p->rb : p->rb;
   p->grid_x = (int)((L.nrt + rows_per_group - 1) / rows_per_group);
   {
-    const int ks = std::min(force_ks, nkt);
+    const int ks = std::min(want_ks, nkt);
     const int per = (nkt + ks - 1) / ks;
     p->ktiles_per_split = per;
     p->ksplit = p->grid_y = (nkt + per - 1) / per;
@@ -335,6 +406,43 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
   return hip_status(ctx, hipGetLastError());
 }
 
+int launch_gemm_rows(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
+                     int64_t n, float ts, float *c, hipStream_t stream) {
+  int rc = NVFP4V_OK;
+  for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
+    const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
+    rc = launch_gemm(ctx, act, mc, k, packed, n, ts, c + r0 * n, stream);
+    act += act_block_bytes(mc, k);
+  }
+  return rc;
+}
+
+int launch_pack_rows(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
+                     hipStream_t stream) {
+  int rc = NVFP4V_OK;
+  for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
+    const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
+    rc = launch_pack_act(ctx, a + r0 * k, mc, k, act, stream);
+    act += act_block_bytes(mc, k);
+  }
+  return rc;
+}
+
+// Workspace checks of the plan of every block of rows of an M-row call.
+static int check_rows_workspace(const nvfp4v_ctx *ctx, const Layout &L, int64_t m) {
+  for (int64_t r0 = 0; r0 < m; r0 += CHUNK_M) {
+    const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
+    Plan p;
+    const int rc = make_plan(ctx, L, mc, &p);
+    if (rc) return rc;
+    if (p.ksplit > 1) {
+      const size_t need = (size_t)p.ksplit * (size_t)mc * (size_t)(L.nrt * ROWS_PER_TILE);
+      if (need > ctx->partial_floats || (size_t)p.nrb > ctx->n_counters) return NVFP4V_E_WORKSPACE;
+    }
+  }
+  return NVFP4V_OK;
+}
+
 }  // namespace nvfp4v
 
 extern "C" size_t nvfp4v_act_packed_bytes(int64_t m, int64_t k) {
@@ -349,7 +457,7 @@ extern "C" int nvfp4v_pack_activations(nvfp4v_ctx *ctx, const uint16_t *a, int64
   if (k < 16 || k % 16 != 0 || k > (int64_t(1) << 22)) return NVFP4V_E_SHAPE;
   if (!aligned16(a) || !aligned16(act)) return NVFP4V_E_ALIGN;
   if (fault_injected()) return NVFP4V_E_FAULT;
-  return launch_pack_act(ctx, a, m, k, (uint8_t *)act, stream);
+  return launch_pack_rows(ctx, a, m, k, (uint8_t *)act, stream);
 }
 
 extern "C" int nvfp4v_verify_gemm_pa(nvfp4v_ctx *ctx, const void *act, int64_t m, int64_t k,
@@ -360,7 +468,10 @@ extern "C" int nvfp4v_verify_gemm_pa(nvfp4v_ctx *ctx, const void *act, int64_t m
   Layout L;
   if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
   if (!aligned16(act) || !aligned16(packed) || !aligned16(c)) return NVFP4V_E_ALIGN;
-  return launch_gemm(ctx, (const uint8_t *)act, m, k, packed, n, ts, c, stream);
+  const int rc = check_rows_workspace(ctx, L, m);
+  if (rc) return rc;
+  if (fault_injected()) return NVFP4V_E_FAULT;
+  return launch_gemm_rows(ctx, (const uint8_t *)act, m, k, packed, n, ts, c, stream);
 }
 
 extern "C" int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k,
@@ -371,18 +482,41 @@ extern "C" int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m,
   Layout L;
   if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
   if (!aligned16(a) || !aligned16(packed) || !aligned16(c)) return NVFP4V_E_ALIGN;
-  if (act_packed_bytes(m, k) > ctx->act_bytes) return NVFP4V_E_WORKSPACE;
-  Plan p;
-  int rc = make_plan(ctx, L, m, &p);
+  if (act_block_bytes(std::min<int64_t>(m, CHUNK_M), k) > ctx->act_bytes) return NVFP4V_E_WORKSPACE;
+  int rc = check_rows_workspace(ctx, L, m);
   if (rc) return rc;
-  if (p.ksplit > 1) {
-    const size_t need = (size_t)p.ksplit * (size_t)m * (size_t)(L.nrt * ROWS_PER_TILE);
-    if (need > ctx->partial_floats || (size_t)p.nrb > ctx->n_counters) return NVFP4V_E_WORKSPACE;
-  }
   if (fault_injected()) return NVFP4V_E_FAULT;
-  rc = launch_pack_act(ctx, a, m, k, ctx->act, stream);
+  // One block of rows at a time through the context's buffer (stream order
+  // keeps a block's GEMM ahead of the next block's packing).
+  for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
+    const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
+    rc = launch_pack_act(ctx, a + r0 * k, mc, k, ctx->act, stream);
+    if (!rc) rc = launch_gemm(ctx, ctx->act, mc, k, packed, n, ts, c + r0 * n, stream);
+  }
+  return rc;
+}
+
+extern "C" int nvfp4v_load_tile_table(nvfp4v_ctx *ctx, const char *path) {
+  if (!ctx) return NVFP4V_E_INVALID_ARG;
+  if (!path) {
+    ctx->n_rules = 0;
+    return NVFP4V_OK;
+  }
+  FILE *f = std::fopen(path, "rb");
+  if (!f) return NVFP4V_E_TABLE;
+  std::string text;
+  char buf[4096];
+  size_t got;
+  while ((got = std::fread(buf, 1, sizeof(buf), f)) > 0 && text.size() < (1u << 20)) text.append(buf, got);
+  std::fclose(f);
+  if (text.size() >= (1u << 20)) return NVFP4V_E_TABLE;
+  TileRule rules[MAX_TILE_RULES];
+  int n = 0;
+  const int rc = parse_tile_table(text.c_str(), rules, &n);
   if (rc) return rc;
-  return launch_gemm(ctx, ctx->act, m, k, packed, n, ts, c, stream);
+  std::memcpy(ctx->rules, rules, sizeof(TileRule) * (size_t)n);
+  ctx->n_rules = n;
+  return NVFP4V_OK;
 }
 
 extern "C" int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64_t m, char *buf,
@@ -391,12 +525,17 @@ extern "C" int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64
   if (m < 1 || m > NVFP4V_MAX_M) return NVFP4V_E_M_RANGE;
   Layout L;
   if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
+  // M > 64 runs one launch per block of 64 rows: describe the first block's
+  // plan and the number of launches.
+  const int64_t blocks = (m + CHUNK_M - 1) / CHUNK_M;
   Plan p;
-  int rc = make_plan(ctx, L, m, &p);
+  int rc = make_plan(ctx, L, std::min<int64_t>(m, CHUNK_M), &p);
   if (rc) return rc;
-  snprintf(buf, len, "mfma16x16x32 %s mblocks=%d r=%d depth=%d waves=%d grid=%dx%d ksplit=%d kt/split=%d lds=%zu exchange=%s",
+  char blk[48] = "";
+  if (blocks > 1) snprintf(blk, sizeof(blk), " launches=%lld (64-row blocks)", (long long)blocks);
+  snprintf(buf, len, "mfma16x16x32 %s mblocks=%d r=%d depth=%d waves=%d grid=%dx%d ksplit=%d kt/split=%d lds=%zu exchange=%s%s",
            p.lds ? "act-in-lds/waves-split-n" : "waves-split-k", p.mblocks, p.rb, p.depth, p.waves,
            p.grid_x, p.grid_y, p.ksplit, p.ktiles_per_split, p.lds_bytes,
-           p.ksplit == 1 ? "none" : p.xcd_local ? "xcd-l2" : "memory");
+           p.ksplit == 1 ? "none" : p.xcd_local ? "xcd-l2" : "memory", blk);
   return NVFP4V_OK;
 }

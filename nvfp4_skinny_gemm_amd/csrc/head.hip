@@ -25,6 +25,7 @@
 // activation fragments stream through a two-deep register ring (loads past
 // the matrix return zeros). E4M3 -> bf16 is exact (4 significant bits, range
 // 2^-9 .. 448): v_cvt_pk_f32_fp8 and the high halves packed with v_perm_b32.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -41,7 +42,7 @@ namespace {
 using namespace nvfp4v::dev;
 
 constexpr int HEAD_TILE_BYTES = 4096;
-constexpr int HEAD_MAX_M = 32;
+constexpr int HEAD_MAX_M = NVFP4V_MAX_M;  // one launch per block of 64 rows
 
 struct HeadArgs {
   const uint8_t *W;      // packed tiles, then the padded row scales
@@ -90,8 +91,16 @@ __device__ inline void compute_htile(const HTile &t, const bf16x8 (&b)[MB][8], f
   }
 }
 
+// Three or four row blocks of activation fragments in a two-deep ring take
+// most of a SIMD's registers: one wave per SIMD there.
+template <int MB>
+constexpr int head_waves_per_simd() {
+  return MB <= 2 ? 2 : 1;
+}
+
 template <int MB, int R>
-__global__ __launch_bounds__(WG_THREADS) void k_head(HeadArgs g) {
+__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(1, head_waves_per_simd<MB>())))
+void k_head(HeadArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rt0 = ((int)blockIdx.x * WG_WAVES + wave) * R;
@@ -180,12 +189,17 @@ int head_r(int mblocks) {
 }
 
 HeadKernel pick_head(int mblocks, int r) {
-  if (mblocks == 1) return r == 1 ? k_head<1, 1> : r == 2 ? k_head<1, 2> : k_head<1, 4>;
-  return r == 1 ? k_head<2, 1> : k_head<2, 2>;
+  switch (mblocks) {
+    case 1: return r == 1 ? k_head<1, 1> : r == 2 ? k_head<1, 2> : k_head<1, 4>;
+    case 2: return r == 1 ? k_head<2, 1> : k_head<2, 2>;
+    case 3: return r == 1 ? k_head<3, 1> : k_head<3, 2>;
+    default: return r == 1 ? k_head<4, 1> : k_head<4, 2>;
+  }
 }
 
-int launch_head(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
-                int64_t n, float *c, hipStream_t stream) {
+// One launch over a block of at most 64 rows (m <= CHUNK_M).
+int launch_head_block(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
+                      int64_t n, float *c, hipStream_t stream) {
   HeadArgs g;
   g.nrt = (int)((n + 15) / 16);
   g.nkt = (int)((k + 255) / 256);
@@ -202,6 +216,18 @@ int launch_head(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
   const int grid = (g.nrt + rows_per_wg - 1) / rows_per_wg;
   hipLaunchKernelGGL(pick_head(mblocks, r), dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, g);
   return hip_status(ctx, hipGetLastError());
+}
+
+// Any m: one launch per block of 64 rows of the packed activations.
+int launch_head(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
+                int64_t n, float *c, hipStream_t stream) {
+  int rc = NVFP4V_OK;
+  for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
+    const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
+    rc = launch_head_block(ctx, act, mc, k, packed, n, c + r0 * n, stream);
+    act += act_block_bytes(mc, k);
+  }
+  return rc;
 }
 
 int head_checks(nvfp4v_ctx *ctx, const void *a, int64_t m, int64_t k, const void *packed, int64_t n,
@@ -284,9 +310,12 @@ extern "C" int nvfp4v_fp8_head_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t 
                                     const void *packed, int64_t n, float *c, hipStream_t stream) {
   int rc = head_checks(ctx, a, m, k, packed, n, c);
   if (rc) return rc;
-  if (act_packed_bytes(m, k) > ctx->act_bytes) return NVFP4V_E_WORKSPACE;
+  if (act_block_bytes(std::min<int64_t>(m, CHUNK_M), k) > ctx->act_bytes) return NVFP4V_E_WORKSPACE;
   if (fault_injected()) return NVFP4V_E_FAULT;
-  rc = launch_pack_act(ctx, a, m, k, ctx->act, stream);
-  if (rc) return rc;
-  return launch_head(ctx, ctx->act, m, k, packed, n, c, stream);
+  for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
+    const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
+    rc = launch_pack_act(ctx, a + r0 * k, mc, k, ctx->act, stream);
+    if (!rc) rc = launch_head_block(ctx, ctx->act, mc, k, packed, n, c + r0 * n, stream);
+  }
+  return rc;
 }

@@ -55,9 +55,21 @@ constexpr int ACT_FRAG_BYTES = 1024;
 // Words of the persistent pass's barrier block (context memory).
 constexpr int PASS_SYNC_WORDS = 1280;
 
-inline size_t act_packed_bytes(int64_t m, int64_t k) {
+// One GEMM launch takes at most CHUNK_M rows. Activations of more rows (a
+// verify pass over several sequences' trees) are packed as consecutive blocks
+// of CHUNK_M rows, the last one shorter, each block in the layout above for
+// its own row count; a GEMM over them runs once per block.
+constexpr int CHUNK_M = 64;
+
+inline size_t act_block_bytes(int64_t m, int64_t k) {
   const int64_t mb = (m + 15) / 16, nkt = (k + 255) / 256;
   return (size_t)nkt * (size_t)mb * 8 * ACT_FRAG_BYTES;
+}
+
+inline size_t act_packed_bytes(int64_t m, int64_t k) {
+  size_t total = 0;
+  for (int64_t r0 = 0; r0 < m; r0 += CHUNK_M) total += act_block_bytes(m - r0 < CHUNK_M ? m - r0 : CHUNK_M, k);
+  return total;
 }
 
 // Byte offset of element (row, col) of A inside the packed activations.
@@ -179,6 +191,16 @@ struct Plan {
   int xcd_local;         // split-K exchange through one XCD's L2 (else through memory)
 };
 
+// One row of a tile table: GEMMs with row tiles in [nrt_lo, nrt_hi], k-tiles
+// in [nkt_lo, nkt_hi] and M in [m_lo, m_hi] take this plan.
+struct TileRule {
+  int nrt_lo, nrt_hi, nkt_lo, nkt_hi, m_lo, m_hi;
+  int lds;     // 1: the LDS-staged variant
+  int r;       // row tiles per work-group (reg) or per wave (lds)
+  int ksplit;  // work-groups along K
+};
+constexpr int MAX_TILE_RULES = 64;
+
 }  // namespace nvfp4v
 
 struct nvfp4v_ctx {
@@ -200,6 +222,11 @@ struct nvfp4v_ctx {
   int last_pass_phases = 0;
   int xcd_local = 0;  // the dispatch probe allows the split-K exchange through one XCD's L2
   unsigned *dev_status = nullptr;  // DEV_STATUS_BYTES: row-block counts of that exchange
+  // Tile table loaded from a file (nvfp4v_load_tile_table), tried before the
+  // built-in one; none when n_rules == 0 (an all-zero context uses the
+  // built-in table).
+  int n_rules = 0;
+  nvfp4v::TileRule rules[nvfp4v::MAX_TILE_RULES];
 };
 
 // Context status lines: 8 lines of DEV_LINE_WORDS words, line x holding the
@@ -217,6 +244,9 @@ int fault_injected();  // NVFP4V_FAULT=launch
 int hip_status(nvfp4v_ctx *ctx, hipError_t e);
 bool aligned16(const void *p);
 int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p);
+// Parse a tile table (text); NVFP4V_E_TABLE if it is malformed, names another
+// arch or a kernel the library does not have.
+int parse_tile_table(const char *text, TileRule *rules, int *n_rules);
 // Sets ctx->xcd_local from a dispatch probe (synchronous; at create).
 int probe_dispatch(nvfp4v_ctx *ctx);
 // Enqueue A (row-major bf16) -> packed activations (no argument checks).
@@ -240,7 +270,13 @@ struct Epilogue {
   uint16_t *rm0 = nullptr, *rm1 = nullptr;  // optional row-major bf16 copies [M][out cols]
   int write_c = 1;
 };
-// Enqueue the GEMM on packed activations (no argument checks).
+// Enqueue the GEMM on packed activations (no argument checks; m <= CHUNK_M).
 int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
                 int64_t n, float ts, float *c, hipStream_t stream, const Epilogue &epi = Epilogue());
+// The same for any m: one launch per block of CHUNK_M rows (plain epilogue).
+int launch_gemm_rows(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
+                     int64_t n, float ts, float *c, hipStream_t stream);
+// Row-major A of any m -> packed activations in blocks of CHUNK_M rows.
+int launch_pack_rows(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
+                     hipStream_t stream);
 }  // namespace nvfp4v

@@ -492,7 +492,7 @@ int chain_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_
     e_d.mode = EPI_PAIR, e_d.c = c2h, e_d.act = a_d;
     e_h.mode = EPI_SCALE, e_h.col0 = 0, e_h.col1 = (int)H, e_h.c = ci, e_h.act = a_next;
     e_h.rm0 = (l == n_layers - 1) ? h_out : nullptr;
-    e_h.rm1 = trace ? trace + (size_t)l * m * H : nullptr;
+    e_h.rm1 = trace ? trace + (size_t)l * w.trace_m * H : nullptr;
     // Only the last layer's fp32 outputs are kept: earlier ones would be overwritten unread.
     e_o.write_c = e_g.write_c = e_d.write_c = e_h.write_c = (l == n_layers - 1) ? 1 : 0;
     rc = launch_gemm(ctx, a_h, m, H, (const uint8_t *)L.qkv, 3 * H, L.ts_qkv, w.C[0], stream, e_o);
@@ -526,12 +526,22 @@ extern "C" int nvfp4v_glue_sum(nvfp4v_ctx *ctx, const float *x, int64_t ldx, con
   return hip_status(ctx, hipGetLastError());
 }
 
+// Workspace of a pass over m rows: one block of rows (at most CHUNK_M) after
+// another, each laid out as pass_ws_layout lays out a pass of its rows.
+static size_t rows_ws_bytes(int64_t m, int64_t hidden, int64_t inter, int n_layers, int64_t upto) {
+  size_t total = 0;
+  for (int64_t r0 = 0; r0 < m && r0 < upto; r0 += CHUNK_M) {
+    PassWs w;
+    total += align256(pass_ws_layout(std::min<int64_t>(CHUNK_M, m - r0), hidden, inter, n_layers, nullptr, &w));
+  }
+  return total;
+}
+
 extern "C" size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter,
                                               int n_layers) {
   if (m < 1 || m > NVFP4V_MAX_M || hidden < 16 || inter < 16 || n_layers < 1) return 0;
   if (hidden % 16 || inter % 16) return 0;
-  PassWs w;
-  return pass_ws_layout(m, hidden, inter, n_layers, nullptr, &w);
+  return rows_ws_bytes(m, hidden, inter, n_layers, m);
 }
 
 extern "C" int nvfp4v_pass_status(nvfp4v_ctx *ctx) {
@@ -550,6 +560,11 @@ extern "C" int nvfp4v_pass_error_site(nvfp4v_ctx *ctx) {
   return (int)site;
 }
 
+// The pass over one block of at most CHUNK_M rows (arguments checked).
+static int verify_pass_block(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_t hidden,
+                             int64_t inter, const uint16_t *h0, int64_t m, void *ws, uint16_t *h_out,
+                             uint16_t *trace, int64_t trace_m, hipStream_t stream);
+
 extern "C" int nvfp4v_verify_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers,
                                   int64_t hidden, int64_t inter, const uint16_t *h0, int64_t m,
                                   void *ws, size_t ws_bytes, uint16_t *h_out, uint16_t *trace,
@@ -567,9 +582,29 @@ extern "C" int nvfp4v_verify_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, i
   for (int l = 0; l < n_layers; ++l)
     if (!layers[l].qkv || !layers[l].o || !layers[l].gate_up || !layers[l].down)
       return NVFP4V_E_INVALID_ARG;
+  if (ws_bytes < rows_ws_bytes(m, hidden, inter, n_layers, m)) return NVFP4V_E_WORKSPACE;
+  // Rows are independent through every GEMM and every glue step, so more
+  // than CHUNK_M rows (several sequences' trees) run as one pass per block of
+  // rows, each on its own part of the workspace.
+  int rc = NVFP4V_OK;
+  for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
+    const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
+    uint8_t *wsb = (uint8_t *)ws + rows_ws_bytes(m, hidden, inter, n_layers, r0);
+    rc = verify_pass_block(ctx, layers, n_layers, hidden, inter, h0 + r0 * hidden, mc, wsb,
+                           h_out + r0 * hidden, trace ? trace + r0 * hidden : nullptr, m, stream);
+  }
+  return rc;
+}
+
+static int verify_pass_block(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_t hidden,
+                             int64_t inter, const uint16_t *h0, int64_t m, void *ws, uint16_t *h_out,
+                             uint16_t *trace, int64_t trace_m, hipStream_t stream) {
+  Layout lq, lo, lg, ld;
+  (void)make_layout(3 * hidden, hidden, &lq), (void)make_layout(hidden, hidden, &lo);
+  (void)make_layout(2 * inter, hidden, &lg), (void)make_layout(hidden, inter, &ld);
   PassWs w;
-  const size_t need = pass_ws_layout(m, hidden, inter, n_layers, (uint8_t *)ws, &w);
-  if (ws_bytes < need) return NVFP4V_E_WORKSPACE;
+  (void)pass_ws_layout(m, hidden, inter, n_layers, (uint8_t *)ws, &w);
+  w.trace_m = trace_m;
   if (hidden % K_PER_TILE || inter % K_PER_TILE) {
     TailArgs t;
     t.act0 = w.act0;
@@ -647,6 +682,7 @@ extern "C" int nvfp4v_verify_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, i
   }
   a.h_out = h_out;
   a.trace = trace;
+  a.trace_m = (int)w.trace_m;
   a.part = ctx->partials;
   a.counters = ctx->counters;
   a.sync = ctx->pass_sync;

@@ -28,6 +28,8 @@ struct PassWs {
   size_t layer_stride;  // bytes between the activation blocks of two layers
   size_t act_off[4];    // offset of phase j's input within a layer's block
   size_t act_bytes[4];
+  int64_t trace_m;      // rows of the trace's [layer][rows][H] layout (the pass's M, or
+                        // the whole call's M when this pass is one block of its rows)
 };
 
 inline size_t pass_ws_layout(int64_t m, int64_t H, int64_t I, int n_layers, uint8_t *base, PassWs *w) {
@@ -53,6 +55,7 @@ inline size_t pass_ws_layout(int64_t m, int64_t H, int64_t I, int n_layers, uint
   w->layer_stride = stride;
   w->act0 = base ? base + off : nullptr;
   off += stride * (size_t)n_layers + align256(w->act_bytes[0]);
+  w->trace_m = m;
   return off;
 }
 
@@ -106,6 +109,7 @@ struct PassArgs {
   int act_bytes[4];
   float *C[4];
   uint16_t *h_out, *trace;
+  int trace_m;  // rows of the trace's [layer][rows][H] layout
   float *part;
   unsigned *counters;
   unsigned *sync;  // barrier words (SYNC_* offsets)
@@ -199,7 +203,7 @@ __device__ inline GemmArgs phase_gemm(const PassArgs &a, int p) {
     e.mode = EPI_SCALE, e.col0 = 0, e.col1 = a.H;
     e.act = blk + a.layer_stride + a.act_off[0];  // next layer's input
     e.rm0 = gl == a.last_layer ? a.h_out : nullptr;
-    e.rm1 = a.trace ? a.trace + (size_t)gl * a.M * a.H : nullptr;
+    e.rm1 = a.trace ? a.trace + (size_t)gl * a.trace_m * a.H : nullptr;
   }
   return g;
 }

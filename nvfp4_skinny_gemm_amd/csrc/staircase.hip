@@ -85,13 +85,13 @@ extern "C" int nvfp4v_staircase(nvfp4v_ctx *ctx, int64_t n, int64_t k, int m_lo,
   // Activations are packed once per M (as the chained pass does); each timed
   // launch is the GEMM kernel alone.
   for (int m = m_lo; e == hipSuccess && rc == NVFP4V_OK && m <= m_hi; ++m) {
-    rc = launch_pack_act(ctx, a, m, k, act, s);
+    rc = launch_pack_rows(ctx, a, m, k, act, s);
     for (int i = 0; i < warmup && rc == NVFP4V_OK; ++i, ++rot)
-      rc = launch_gemm(ctx, act, m, k, w + (rot % copies) * stride, n, 1.0f, c, s);
+      rc = launch_gemm_rows(ctx, act, m, k, w + (rot % copies) * stride, n, 1.0f, c, s);
     for (int i = 0; i < reps && rc == NVFP4V_OK; ++i, ++rot) {
       e = hipEventRecord(ev[2 * i], s);
       if (e != hipSuccess) break;
-      rc = launch_gemm(ctx, act, m, k, w + (rot % copies) * stride, n, 1.0f, c, s);
+      rc = launch_gemm_rows(ctx, act, m, k, w + (rot % copies) * stride, n, 1.0f, c, s);
       if (rc != NVFP4V_OK) break;
       e = hipEventRecord(ev[2 * i + 1], s);
       if (e != hipSuccess) break;

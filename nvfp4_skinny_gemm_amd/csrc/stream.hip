@@ -700,6 +700,7 @@ int stream_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64
   }
   a.h_out = h_out;
   a.trace = trace;
+  a.trace_m = (int)w.trace_m;
   a.part = ctx->partials;
   a.counters = ctx->counters;
   a.sync = ctx->pass_sync;

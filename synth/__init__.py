@@ -30,7 +30,7 @@ import hashlib
 import numpy as np
 
 ROW_BLOCK = 256
-MAX_ROWS = 64  # activations are drawn as 64 rows; callers slice the first M
+MAX_ROWS = 128  # activations are drawn as 128 rows (row i is the same for any M); callers slice
 
 
 def _key(seed: int, tag: str, *ids: int) -> int:

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_strerror(lib):
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         assert nv.strerror(code) and nv.strerror(code) != "unknown status"
     assert nv.strerror(-99) == "unknown status"
 
@@ -86,7 +86,7 @@ def test_verify_gemm_argument_errors(lib):
     assert f(ctx, a, 8, 256, None, 512, 1.0, c, None) == nv.E_INVALID_ARG
     assert f(ctx, a, 8, 256, w, 512, 1.0, None, None) == nv.E_INVALID_ARG
     assert f(ctx, a, 0, 256, w, 512, 1.0, c, None) == nv.E_M_RANGE
-    assert f(ctx, a, 65, 256, w, 512, 1.0, c, None) == nv.E_M_RANGE
+    assert f(ctx, a, 129, 256, w, 512, 1.0, c, None) == nv.E_M_RANGE
     assert f(ctx, a, 8, 250, w, 512, 1.0, c, None) == nv.E_SHAPE
     assert f(ctx, a, 8, 0, w, 512, 1.0, c, None) == nv.E_SHAPE
     assert f(ctx, a, 8, 256, w, 0, 1.0, c, None) == nv.E_SHAPE
@@ -102,7 +102,7 @@ def test_fault_injection(lib, monkeypatch):
     ctx = FakeCtx().ptr
     monkeypatch.setenv("NVFP4V_FAULT", "launch")
     out = ctypes.c_void_p()
-    assert lib.nvfp4v_create(ctypes.byref(out), 0) == nv.E_FAULT
+    assert lib.nvfp4v_create(ctypes.byref(out), 0, None) == nv.E_FAULT
     assert lib.nvfp4v_pack(ctx, fake_dev(), fake_dev(), 16, 128, fake_dev(0x40000), None) == nv.E_FAULT
     assert lib.nvfp4v_quantize(ctx, fake_dev(), 16, 128, fake_dev(), fake_dev(), None) == nv.E_FAULT
     assert lib.nvfp4v_staircase(ctx, 16, 128, 1, 2, 0, 1, 0, fake_dev()) == nv.E_FAULT
@@ -111,9 +111,9 @@ def test_fault_injection(lib, monkeypatch):
 @host_only
 def test_other_argument_errors(lib):
     ctx = FakeCtx().ptr
-    assert lib.nvfp4v_create(None, 0) == nv.E_INVALID_ARG
+    assert lib.nvfp4v_create(None, 0, None) == nv.E_INVALID_ARG
     out = ctypes.c_void_p()
-    assert lib.nvfp4v_create(ctypes.byref(out), -1) == nv.E_INVALID_ARG
+    assert lib.nvfp4v_create(ctypes.byref(out), -1, None) == nv.E_INVALID_ARG
     assert lib.nvfp4v_pack(ctx, fake_dev(), fake_dev(), 16, 100, fake_dev(), None) == nv.E_SHAPE
     assert lib.nvfp4v_pack(ctx, fake_dev(), fake_dev(), 16, 128, fake_dev(0x1001), None) == nv.E_ALIGN
     assert lib.nvfp4v_unpack(ctx, fake_dev(0x1004), 16, 128, fake_dev(), fake_dev(), None) == nv.E_ALIGN
@@ -121,7 +121,7 @@ def test_other_argument_errors(lib):
     us = (ctypes.c_double * 4)()
     assert lib.nvfp4v_staircase(ctx, 16, 128, 0, 2, 0, 1, 0, us) == nv.E_M_RANGE
     assert lib.nvfp4v_staircase(ctx, 16, 128, 3, 2, 0, 1, 0, us) == nv.E_M_RANGE
-    assert lib.nvfp4v_staircase(ctx, 16, 128, 1, 65, 0, 1, 0, us) == nv.E_M_RANGE
+    assert lib.nvfp4v_staircase(ctx, 16, 128, 1, 129, 0, 1, 0, us) == nv.E_M_RANGE
     assert lib.nvfp4v_staircase(ctx, 16, 128, 1, 2, 0, 0, 0, us) == nv.E_INVALID_ARG
     buf = ctypes.create_string_buffer(8)
     assert lib.nvfp4v_describe_plan(ctx, 16, 128, 0, buf, 8) == nv.E_M_RANGE
@@ -211,3 +211,71 @@ def test_fp8_head_argument_errors(lib):
     assert lib.nvfp4v_fp8_head_gemm_pa(None, None, 1, 16, None, 1, None, None) == nv.E_INVALID_ARG
     with pytest.raises(nv.Nvfp4vError):
         nv.fp8_pack_host(np.zeros((2, 24), np.uint8), np.zeros(2, np.float32))
+
+
+TABLE_PATH = os.path.join(os.path.dirname(nv.__file__), "tables", "gfx950.txt")
+
+
+def plan(lib, ctx, n, k, m):
+    buf = ctypes.create_string_buffer(256)
+    assert lib.nvfp4v_describe_plan(ctx, n, k, m, buf, 256) == nv.OK
+    return buf.value.decode()
+
+
+def test_tile_table_file_changes_the_plan(lib, tmp_path):
+    """A table file loaded into a context changes its plans for the GEMMs its
+    rules hold and leaves the others on the built-in table; NULL goes back."""
+    ctx = FakeCtx().ptr
+    base_o, base_down = plan(lib, ctx, 5120, 5120, 16), plan(lib, ctx, 5120, 17408, 16)
+    assert "r=2 " in base_o and "ksplit=1" in base_o
+    f = tmp_path / "o_only.txt"
+    f.write_text("arch gfx950\n# o at 9..16 rows on one R = 8 work-group per 8 row tiles, 2 K pieces\n"
+                 "rule 300 330 10 30 9 16 reg 8 2\n")
+    assert lib.nvfp4v_load_tile_table(ctx, str(f).encode()) == nv.OK
+    got = plan(lib, ctx, 5120, 5120, 16)
+    assert "r=8 " in got and "ksplit=2" in got and got != base_o
+    assert plan(lib, ctx, 5120, 5120, 8) == plan(lib, FakeCtx().ptr, 5120, 5120, 8)  # M outside the rule
+    assert plan(lib, ctx, 5120, 17408, 16) == base_down  # another shape
+    assert lib.nvfp4v_load_tile_table(ctx, None) == nv.OK
+    assert plan(lib, ctx, 5120, 5120, 16) == base_o
+
+
+def test_checked_in_table_is_the_built_in_one(lib):
+    """Loading tables/gfx950.txt (the file the build compiles in) changes no plan."""
+    ctx, ref = FakeCtx().ptr, FakeCtx().ptr
+    assert lib.nvfp4v_load_tile_table(ctx, TABLE_PATH.encode()) == nv.OK
+    for n, k in ((151936, 5120), (15360, 5120), (5120, 5120), (34816, 5120), (5120, 17408), (17408, 5120),
+                 (512, 256), (10240, 5120)):
+        for m in (1, 8, 9, 16, 17, 32, 33, 48, 49, 64):
+            assert plan(lib, ctx, n, k, m) == plan(lib, ref, n, k, m), (n, k, m)
+
+
+@pytest.mark.parametrize("text", [
+    "rule 1 * 1 * 1 64 reg 2 1\n",                    # no arch line
+    "arch gfx942\nrule 1 * 1 * 1 64 reg 2 1\n",       # another arch
+    "arch gfx950\nrule 1 * 1 * 1 64 wmma 2 1\n",      # unknown kernel
+    "arch gfx950\nrule 1 * 1 * 1 64 reg 3 1\n",       # R with no kernel
+    "arch gfx950\nrule 1 * 1 * 1 64 lds 2 1\n",       # lds R = 2 is built up to 32 rows only
+    "arch gfx950\nrule 1 * 1 * 1 65 reg 2 1\n",       # M beyond the API's range
+    "arch gfx950\nrule 5 4 1 * 1 64 reg 2 1\n",       # empty range
+    "arch gfx950\nrule 1 * 1 * 1 64 reg 2 0\n",       # no K split
+    "arch gfx950\nrule 1 * 1 * 1 64 reg 2\n",         # missing field
+    "arch gfx950\nrule 1 * 1 * x 64 reg 2 1\n",       # not a number
+    "arch gfx950\n" + "rule 1 * 1 * 1 64 reg 2 1\n" * 65,  # too many rules
+], ids=["no-arch", "arch", "kernel", "r", "lds-r", "m", "range", "ks", "fields", "number", "count"])
+def test_bad_tile_table_is_refused(lib, tmp_path, text):
+    ctx = FakeCtx().ptr
+    f = tmp_path / "bad.txt"
+    f.write_text(text)
+    before = plan(lib, ctx, 5120, 5120, 16)
+    assert lib.nvfp4v_load_tile_table(ctx, str(f).encode()) == nv.E_TABLE
+    assert plan(lib, ctx, 5120, 5120, 16) == before  # the previous table stays
+    out = ctypes.c_void_p()
+    assert lib.nvfp4v_create(ctypes.byref(out), 0, str(f).encode()) == nv.E_TABLE
+    assert not out.value
+
+
+def test_missing_tile_table_file(lib, tmp_path):
+    ctx = FakeCtx().ptr
+    assert lib.nvfp4v_load_tile_table(ctx, str(tmp_path / "none.txt").encode()) == nv.E_TABLE
+    assert lib.nvfp4v_load_tile_table(None, None) == nv.E_INVALID_ARG

@@ -49,10 +49,12 @@ def check(oracle, c_gpu, c_ref, s_ref, label):
                                 c_ref[i, j], s_ref[i, j]))
 
 
-# Several row tiles and k-tiles with ragged tails (N % 16, K % 256), one- and
-# two-row-block M, and the degenerate single row / single 16-wide k-block.
+# Several row tiles and k-tiles with ragged tails (N % 16, K % 256), one to
+# four row blocks of M and two blocks of 64 rows (M = 100), and the degenerate
+# single row / single 16-wide k-block.
 @pytest.mark.parametrize("n,k,m", [(1, 16, 1), (17, 48, 5), (100, 272, 16), (33, 1040, 17),
-                                   (64, 512, 32), (250, 784, 7), (129, 2064, 24)])
+                                   (64, 512, 32), (250, 784, 7), (129, 2064, 24), (250, 784, 48),
+                                   (129, 2064, 100)])
 def test_head_parity_quantised(torch_cuda, ctx, oracle_mod, n, k, m):
     torch = torch_cuda
     log("head parity n=%d k=%d m=%d" % (n, k, m))
@@ -100,7 +102,7 @@ def full_head(torch_cuda):
     return n, k, codes, scales, packed
 
 
-@pytest.mark.parametrize("m", [1, 16, 32])
+@pytest.mark.parametrize("m", [1, 16, 32, 64, 128])
 def test_head_full_size_sampled(torch_cuda, ctx, oracle_mod, full_head, m):
     """The LM head of the 27B stack, 151936 x 5120, at the tree sizes: random
     finite E4M3 codes and row scales; 640 sampled rows (both ends included)
@@ -120,7 +122,7 @@ def test_head_full_size_sampled(torch_cuda, ctx, oracle_mod, full_head, m):
 def test_head_argument_errors(torch_cuda, ctx):
     torch = torch_cuda
     packed = torch.zeros(nv.fp8_packed_bytes(32, 256), dtype=torch.uint8, device="cuda")
-    a = torch.zeros((33, 256), dtype=torch.bfloat16, device="cuda")
+    a = torch.zeros((129, 256), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(nv.Nvfp4vError) as e:
         ctx.fp8_head_gemm(a, packed, 32, 256)
     assert e.value.status == nv.E_M_RANGE

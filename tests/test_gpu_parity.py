@@ -182,7 +182,8 @@ def full_shape_case(torch, ctx, oracle_mod, n, k, ms, stream):
 def test_gate_up_projection_full(torch_cuda, ctx, oracle_mod):
     # every regime of the tile table: up to 8 rows, 9..16 (the LDS-staged K split
     # from 1024 row tiles), 17..32, 33..48 and 49..64
-    full_shape_case(torch_cuda, ctx, oracle_mod, 17408, 5120, [1, 8, 9, 16, 24, 32, 33, 49, 64], "gate_up")
+    full_shape_case(torch_cuda, ctx, oracle_mod, 17408, 5120, [1, 8, 9, 16, 24, 32, 33, 49, 64, 65, 96, 128],
+                    "gate_up")
 
 
 def test_square_projection_full(torch_cuda, ctx, oracle_mod):
@@ -192,10 +193,10 @@ def test_square_projection_full(torch_cuda, ctx, oracle_mod):
 
 def test_down_projection_full(torch_cuda, ctx, oracle_mod):
     torch = torch_cuda
-    packed, a_dev, outs = full_shape_case(torch, ctx, oracle_mod, 5120, 17408, [1, 8, 9, 16, 24, 32, 33, 64],
-                                          "down")
+    packed, a_dev, outs = full_shape_case(torch, ctx, oracle_mod, 5120, 17408,
+                                          [1, 8, 9, 16, 24, 32, 33, 64, 65, 96, 128], "down")
     # determinism: the same call again is bitwise identical
-    for m in (1, 16, 32):
+    for m in (1, 16, 32, 128):
         c2 = ctx.verify_gemm(a_dev[:m], packed, 5120, 17408).cpu().numpy()
         assert np.array_equal(c2.view(np.uint32), outs[m].view(np.uint32)), "M=%d not deterministic" % m
 
@@ -217,12 +218,12 @@ def test_lm_head_sampled(torch_cuda, ctx, oracle_mod):
     assert np.array_equal(scales_d[idx].cpu().numpy(), osc)
     packed = ctx.pack(codes_d, scales_d, n, k)
     del codes_d, scales_d
-    a = synth.activations_bf16(64, k, seed=0, stream="head/act", outliers=True)
+    a = synth.activations_bf16(128, k, seed=0, stream="head/act", outliers=True)
     c_ref, s_ref = oracle_mod.gemm(a, oc, osc)
     a_dev = bf16_dev(torch, a)
     # every tile-table regime of the head: one row block (LDS-staged, R = 2),
-    # two, three (33..48) and four row blocks
-    for m in (1, 16, 17, 32, 33, 40, 48, 64):
+    # two, three (33..48) and four row blocks; beyond 64 rows, blocks of 64
+    for m in (1, 16, 17, 32, 33, 40, 48, 64, 96, 128):
         log("head M=%d plan: %s" % (m, ctx.describe_plan(n, k, m)))
         c = ctx.verify_gemm(a_dev[:m], packed, n, k)
         assert_parity(oracle_mod, c[:, idx].cpu().numpy(), c_ref[:m], s_ref[:m], "head M=%d" % m)

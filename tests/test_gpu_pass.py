@@ -111,7 +111,7 @@ def mode_ctx(ctx, request):
 
 
 @pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
-@pytest.mark.parametrize("m", [1, 8, 16, 33, 64])
+@pytest.mark.parametrize("m", [1, 8, 16, 33, 64, 65, 128])
 def test_pass_equals_composition(torch_cuda, mode_ctx, m):
     torch, ctx = torch_cuda, mode_ctx
     H, I, L = 256, 512, 3
