@@ -284,9 +284,11 @@ def parse_sweep(s):
     return out
 
 
-def find_steps(us, m0=1):
+def find_steps(us, m0=1, persist=2):
     """Staircase steps: M where the time exceeds 1.03x the median of the plateau
-    of preceding M values by more than 3 MADs of that plateau's noise."""
+    of preceding M values by more than 3 MADs of that plateau's noise, and the
+    next `persist` M values (where measured) stay above that threshold too, so
+    a single noisy point is not a step."""
     import numpy as np
 
     steps, start = [], 0
@@ -294,7 +296,8 @@ def find_steps(us, m0=1):
         plateau = np.asarray(us[start:i])
         med = float(np.median(plateau))
         mad = float(np.median(np.abs(plateau - med))) if len(plateau) > 1 else 0.0
-        if us[i] > 1.03 * med and us[i] - med > 3 * mad:
+        thr = max(1.03 * med, med + 3 * mad)
+        if us[i] > thr and all(u > thr for u in us[i + 1:i + 1 + persist]):
             steps.append(m0 + i)
             start = i
     return steps

@@ -248,11 +248,13 @@ int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64_t m, char 
  * research page, "What it says"). The call allocates its own buffers:
  * max(1, ceil(rotate_bytes / packed)) weight copies filled with valid random
  * codes and scales, cycled so timing does not hit a cache-resident copy; it
- * runs `warmup` untimed launches, then `reps` launches each between a pair of
- * HIP events on an internal stream, and writes the median duration in
- * microseconds to us_out[M - m_lo]. The activations are packed once per M
- * (as the chained pass does), so each timed launch is the GEMM kernel alone.
- * Synchronous. */
+ * runs `warmup` untimed launches, then five batches of `reps` back-to-back
+ * launches, each batch between one pair of HIP events on an internal stream,
+ * and writes the median batch's time per launch in microseconds to
+ * us_out[M - m_lo] (a pair of events around one launch would add a launch's
+ * dispatch latency). The activations are packed once per M (as the chained
+ * pass does), so the timed launches are the GEMM kernel alone (M > 64: one
+ * launch per block of 64 rows, counted together). Synchronous. */
 int nvfp4v_staircase(nvfp4v_ctx *ctx, int64_t n, int64_t k, int m_lo, int m_hi, int warmup,
                      int reps, size_t rotate_bytes, double *us_out);
 

@@ -66,7 +66,12 @@ extern "C" int nvfp4v_staircase(nvfp4v_ctx *ctx, int64_t n, int64_t k, int m_lo,
   uint16_t *a = nullptr;
   float *c = nullptr;
   hipStream_t s = nullptr;
-  std::vector<hipEvent_t> ev((size_t)reps * 2, nullptr);
+  // Each M is timed as `reps` back-to-back launches between one pair of events,
+  // repeated over `rounds` batches, and the median batch is kept: a pair of
+  // events around a single launch would add the dispatch latency of a launch
+  // from an idle queue (about 6 us) to the kernel's duration.
+  constexpr int rounds = 5;
+  std::vector<hipEvent_t> ev((size_t)rounds * 2, nullptr);
   int rc = NVFP4V_OK;
   hipError_t e = hipMalloc((void **)&w, stride * copies);
   if (e == hipSuccess) e = hipMalloc((void **)&a, (size_t)NVFP4V_MAX_M * (size_t)k * 2);
@@ -83,30 +88,27 @@ extern "C" int nvfp4v_staircase(nvfp4v_ctx *ctx, int64_t n, int64_t k, int m_lo,
   }
   size_t rot = 0;
   // Activations are packed once per M (as the chained pass does); each timed
-  // launch is the GEMM kernel alone.
+  // launch is the GEMM alone (M > 64: one launch per block of 64 rows).
   for (int m = m_lo; e == hipSuccess && rc == NVFP4V_OK && m <= m_hi; ++m) {
     rc = launch_pack_rows(ctx, a, m, k, act, s);
     for (int i = 0; i < warmup && rc == NVFP4V_OK; ++i, ++rot)
       rc = launch_gemm_rows(ctx, act, m, k, w + (rot % copies) * stride, n, 1.0f, c, s);
-    for (int i = 0; i < reps && rc == NVFP4V_OK; ++i, ++rot) {
-      e = hipEventRecord(ev[2 * i], s);
-      if (e != hipSuccess) break;
-      rc = launch_gemm_rows(ctx, act, m, k, w + (rot % copies) * stride, n, 1.0f, c, s);
-      if (rc != NVFP4V_OK) break;
-      e = hipEventRecord(ev[2 * i + 1], s);
-      if (e != hipSuccess) break;
+    for (int b = 0; b < rounds && rc == NVFP4V_OK && e == hipSuccess; ++b) {
+      e = hipEventRecord(ev[2 * b], s);
+      for (int i = 0; i < reps && rc == NVFP4V_OK && e == hipSuccess; ++i, ++rot)
+        rc = launch_gemm_rows(ctx, act, m, k, w + (rot % copies) * stride, n, 1.0f, c, s);
+      if (e == hipSuccess && rc == NVFP4V_OK) e = hipEventRecord(ev[2 * b + 1], s);
     }
     if (e == hipSuccess && rc == NVFP4V_OK) e = hipStreamSynchronize(s);
     if (e == hipSuccess && rc == NVFP4V_OK) {
-      std::vector<double> t((size_t)reps);
-      for (int i = 0; i < reps && e == hipSuccess; ++i) {
+      std::vector<double> t((size_t)rounds);
+      for (int b = 0; b < rounds && e == hipSuccess; ++b) {
         float ms = 0.f;
-        e = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]);
-        t[(size_t)i] = 1000.0 * (double)ms;
+        e = hipEventElapsedTime(&ms, ev[2 * b], ev[2 * b + 1]);
+        t[(size_t)b] = 1000.0 * (double)ms / reps;
       }
       std::sort(t.begin(), t.end());
-      us_out[m - m_lo] = reps % 2 ? t[(size_t)reps / 2]
-                                  : 0.5 * (t[(size_t)reps / 2 - 1] + t[(size_t)reps / 2]);
+      us_out[m - m_lo] = t[(size_t)rounds / 2];
     }
   }
   if (e != hipSuccess && rc == NVFP4V_OK) rc = hip_status(ctx, e);
