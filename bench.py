@@ -34,8 +34,7 @@ BYTES_PER_WEIGHT = 0.5625  # 4-bit code + one E4M3 byte per 16 weights
 PEAK_HBM_GBS = 8000.0
 METRIC = "verify-pass µs and achieved HBM GB/s vs M (1..32), full 27B layer stack"
 # Pass schedules (nvfp4v_set_pass_mode) by name.
-SCHEDULES = {"chain": "PASS_CHAIN", "persistent": "PASS_PERSISTENT", "flow": "PASS_FLOW",
-             "stream": "PASS_STREAM"}
+SCHEDULES = {"chain": "PASS_CHAIN", "persistent": "PASS_PERSISTENT"}
 PAGES_CONTEXT = {"hardware": "DGX Spark GB10 (other machine; whole forward pass incl. attention)",
                  "verify_pass_ms": {"8": 75.5, "16": 74.4, "24": 83.1, "32": 87.8}}
 
@@ -355,7 +354,7 @@ def main():
     ap.add_argument("--m", type=int, default=16)
     ap.add_argument("--mode", choices=tuple(SCHEDULES), default="chain",
                     help="pass schedule of the headline number")
-    ap.add_argument("--compare", default="stream",
+    ap.add_argument("--compare", default="persistent",
                     help="comma-separated schedules timed beside the headline one ('' = none)")
     ap.add_argument("--sweep", default="1-32", help="M values for the per-M pass staircase ('' = none)")
     ap.add_argument("--sweep-steps", type=int, default=5)

@@ -341,28 +341,13 @@ size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter, int
  *                           stream-ordered;
  *   NVFP4V_PASS_PERSISTENT  one cooperatively launched persistent kernel per
  *                           32 layers whose work-groups meet at a grid barrier
- *                           between dependent GEMMs;
- *   NVFP4V_PASS_FLOW        one cooperatively launched persistent kernel per
- *                           32 layers in which a producer wave per work-group
- *                           streams weights into LDS across GEMM boundaries
- *                           while its consumer waves compute (M <= 32; larger
- *                           M runs the chained launches);
- *   NVFP4V_PASS_STREAM      one cooperatively launched persistent kernel per
- *                           32 layers, one work-group per CU, each with an
- *                           equal rectangle of every GEMM: a weight wave
- *                           streams tiles into a large LDS ring without ever
- *                           waiting at a GEMM boundary, an activation wave
- *                           loads each activation k-tile once and runs the
- *                           grid barrier, and four consumer waves dequantise
- *                           and multiply; split-K partials meet in one XCD's
- *                           L2 (M <= 32; larger M runs the chained launches).
- * Each mode is deterministic (equal inputs give equal bits on every call); the
- * modes split K differently, so their fp32 sums can differ in the last bits.
+ *                           between dependent GEMMs.
+ * Both modes are deterministic (equal inputs give equal bits on every call);
+ * at some shapes they split K differently, so their fp32 sums can differ in
+ * the last bits.
  * Errors: INVALID_ARG. */
 #define NVFP4V_PASS_CHAIN 0
 #define NVFP4V_PASS_PERSISTENT 1
-#define NVFP4V_PASS_FLOW 2
-#define NVFP4V_PASS_STREAM 3
 int nvfp4v_set_pass_mode(nvfp4v_ctx *ctx, int mode);
 int nvfp4v_get_pass_mode(const nvfp4v_ctx *ctx);
 
@@ -379,7 +364,7 @@ int nvfp4v_get_pass_mode(const nvfp4v_ctx *ctx);
  * glue step runs in the epilogue of the GEMM that produces its input; fp32
  * outputs are written for the last layer only (earlier ones would be
  * overwritten unread). In
- * the persistent and flow modes a barrier wait that exceeds 2 s (it cannot while the launch
+ * the persistent mode a barrier wait that exceeds 2 s (it cannot while the launch
  * is co-resident) ends the kernel early and sets an error flag that
  * nvfp4v_pass_status reports; the outputs are then undefined. After the call returns, the
  * workspace holds the last layer's fp32 GEMM outputs (qkv [M][3H] at offset 0,
@@ -397,12 +382,8 @@ int nvfp4v_verify_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers
  * context finished (NVFP4V_OK) or gave up at a barrier (NVFP4V_E_TIMEOUT). */
 int nvfp4v_pass_status(nvfp4v_ctx *ctx);
 /* Synchronise and return where the last persistent pass gave up: 0 if it did
- * not, 1 at a grid barrier, 16..24 at one of the stream schedule's bounded
- * waits (16: work-group places on the XCDs, 17: a free weight slot, 18: a free
- * activation slot, 19: the consumers' end of a phase, 20: an activation
- * k-tile, 21: a weight tile, 22: split-K partials, 23: the end of the last
- * phase, 24: another wave gave up first). For diagnosis; nvfp4v_pass_status
- * reports the failure itself. Errors: INVALID_ARG, HIP. */
+ * not, 1 at a grid barrier. For diagnosis; nvfp4v_pass_status reports the
+ * failure itself. Errors: INVALID_ARG, HIP. */
 int nvfp4v_pass_error_site(nvfp4v_ctx *ctx);
 /* Work-groups of the last persistent pass launch (0 before the first). */
 int nvfp4v_last_pass_grid(const nvfp4v_ctx *ctx);

@@ -30,8 +30,6 @@ E_DISPATCH = -10
 E_TABLE = -11
 PASS_CHAIN = 0
 PASS_PERSISTENT = 1
-PASS_FLOW = 2
-PASS_STREAM = 3
 MAX_M = 128
 
 _lib = None
@@ -472,7 +470,7 @@ class Context:
         return int(load().nvfp4v_pass_error_site(self._h))
 
     def set_pass_mode(self, mode: int) -> None:
-        """PASS_CHAIN (four GEMM launches per layer), PASS_PERSISTENT or PASS_FLOW."""
+        """PASS_CHAIN (four GEMM launches per layer) or PASS_PERSISTENT."""
         _check(load().nvfp4v_set_pass_mode(self._h, int(mode)), "set_pass_mode")
 
     def get_pass_mode(self) -> int:

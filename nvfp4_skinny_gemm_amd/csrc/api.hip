@@ -121,8 +121,7 @@ extern "C" size_t nvfp4v_ctx_size(void) { return sizeof(nvfp4v_ctx); }
 extern "C" int nvfp4v_last_hip_error(const nvfp4v_ctx *ctx) { return ctx ? ctx->last_hip : 0; }
 
 extern "C" int nvfp4v_set_pass_mode(nvfp4v_ctx *ctx, int mode) {
-  if (!ctx || (mode != NVFP4V_PASS_CHAIN && mode != NVFP4V_PASS_PERSISTENT && mode != NVFP4V_PASS_FLOW &&
-               mode != NVFP4V_PASS_STREAM))
+  if (!ctx || (mode != NVFP4V_PASS_CHAIN && mode != NVFP4V_PASS_PERSISTENT))
     return NVFP4V_E_INVALID_ARG;
   ctx->pass_mode = mode;
   return NVFP4V_OK;

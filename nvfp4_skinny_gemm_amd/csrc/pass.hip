@@ -626,19 +626,6 @@ static int verify_pass_block(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_
     if (rc) return rc;
   }
   if (ctx->pass_mode == NVFP4V_PASS_CHAIN) return chain_pass(ctx, layers, n_layers, hidden, inter, h0, m, w, h_out, trace, stream);
-  if (ctx->pass_mode == NVFP4V_PASS_STREAM) {
-    // Rows beyond 32 keep the chained launches (two row blocks of activation
-    // fragments and accumulators per consumer wave is the most the stream
-    // kernel is built for).
-    if (m > 32) return chain_pass(ctx, layers, n_layers, hidden, inter, h0, m, w, h_out, trace, stream);
-    return stream_pass(ctx, layers, n_layers, hidden, inter, h0, m, w, h_out, trace, stream);
-  }
-  if (ctx->pass_mode == NVFP4V_PASS_FLOW) {
-    // Rows beyond 32 keep the chained launches (two row blocks of activation
-    // fragments per consumer wave is the most the flow kernel is built for).
-    if (m > 32) return chain_pass(ctx, layers, n_layers, hidden, inter, h0, m, w, h_out, trace, stream);
-    return flow_pass(ctx, layers, n_layers, hidden, inter, h0, m, w, h_out, trace, stream);
-  }
 
   const int mb = (int)((m + 15) / 16);
   int target_per_cu = 0, pr = 0;

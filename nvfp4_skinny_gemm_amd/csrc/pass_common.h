@@ -1,6 +1,5 @@
-// Declarations shared by the two persistent pass kernels (pass.hip: one
-// barrier per phase with a register ring per wave; flow.hip: a producer wave
-// streaming weights into an LDS ring across phases) and the chained launches:
+// Declarations shared by the persistent pass kernel (pass.hip: one grid
+// barrier per phase with a register ring per wave) and the chained launches:
 // the pass workspace, the kernel arguments, the grid barrier and the fused
 // epilogue of each phase. The stack and its glue are described in pass.hip.
 #pragma once
@@ -73,32 +72,12 @@ struct PhaseShape {
   int rows_rem;  // rem * R * 16: rows covered by the split row blocks
 };
 
-// Work of one phase in flow mode (flow.hip): the phase's row blocks of RT
-// row tiles times its k-tiles, T units taken in row-block-major order, cut
-// into G equal contiguous ranges, one per work-group.
-struct FlowShape {
-  int nrt, nkt, nrb;
-  int64_t T;   // nrb * nkt
-  int nq_max;  // most work-groups any row block is spread over
-};
-
-// Work of one projection in stream mode (stream.hip): the grid's G
-// work-groups form G / gk row groups of R row tiles, each cut along K into gk
-// k-groups of S k-tiles; the gk work-groups of a row group run on one XCD.
-// unit = 2 when the row tiles come in (gate, up) pairs.
-struct StreamShape {
-  int gk, R, S, unit;
-};
-
 struct PassArgs {
   int n_layers;    // layers in this launch (<= LAYERS_PER_LAUNCH)
   int M;
   int layer0;      // index of this launch's first layer in the whole stack
   int last_layer;  // index of the stack's last layer
   PhaseShape ph[4];
-  FlowShape fs[4];
-  StreamShape ss[4];
-  int cus_per_xcd;  // stream mode: work-groups per XCD (the grid is 8 times that)
   const uint8_t *w[LAYERS_PER_LAUNCH][4];
   float ts[LAYERS_PER_LAUNCH][4];
   float cst[4];  // glue constants: H^-1/2, H^-1/2, (2H)^-1/2, I^-1/2
@@ -207,16 +186,6 @@ __device__ inline GemmArgs phase_gemm(const PassArgs &a, int p) {
   }
   return g;
 }
-
-// The pass in stream mode (stream.hip): one cooperative launch per 32 layers.
-int stream_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_t H, int64_t I,
-                const uint16_t *h0, int64_t m, const PassWs &w, uint16_t *h_out, uint16_t *trace,
-                hipStream_t stream);
-
-// The pass in flow mode (flow.hip): one cooperative launch per 32 layers.
-int flow_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_t H, int64_t I,
-              const uint16_t *h0, int64_t m, const PassWs &w, uint16_t *h_out, uint16_t *trace,
-              hipStream_t stream);
 
 }  // namespace passk
 }  // namespace nvfp4v

@@ -279,3 +279,17 @@ def test_missing_tile_table_file(lib, tmp_path):
     ctx = FakeCtx().ptr
     assert lib.nvfp4v_load_tile_table(ctx, str(tmp_path / "none.txt").encode()) == nv.E_TABLE
     assert lib.nvfp4v_load_tile_table(None, None) == nv.E_INVALID_ARG
+
+
+def test_pass_modes():
+    """Two schedules, chain (0, the default) and persistent (1); any other mode
+    is rejected and leaves the context's mode unchanged."""
+    lib = nv.load()
+    ctx = FakeCtx().ptr
+    assert lib.nvfp4v_get_pass_mode(ctx) == nv.PASS_CHAIN
+    assert lib.nvfp4v_set_pass_mode(ctx, nv.PASS_PERSISTENT) == nv.OK
+    assert lib.nvfp4v_get_pass_mode(ctx) == nv.PASS_PERSISTENT
+    for bad in (-1, 2, 3, 99):
+        assert lib.nvfp4v_set_pass_mode(ctx, bad) == nv.E_INVALID_ARG
+        assert lib.nvfp4v_get_pass_mode(ctx) == nv.PASS_PERSISTENT
+    assert lib.nvfp4v_set_pass_mode(None, nv.PASS_CHAIN) == nv.E_INVALID_ARG

@@ -96,11 +96,6 @@ def manual_chain(torch, ctx, packed, h0, H, I):
 
 
 MODES = [pytest.param(nv.PASS_CHAIN, id="chain"), pytest.param(nv.PASS_PERSISTENT, id="persistent")]
-# The flow and stream schedules cut K at other points than single calls do, so
-# they are checked against the oracle (and for determinism), not bitwise
-# against them.
-CUT_MODES = [pytest.param(nv.PASS_FLOW, id="flow"), pytest.param(nv.PASS_STREAM, id="stream")]
-ALL_MODES = MODES + CUT_MODES
 
 
 @pytest.fixture
@@ -178,7 +173,7 @@ def test_pass_longer_than_one_launch(torch_cuda, mode_ctx):
     assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16))
 
 
-@pytest.mark.parametrize("mode_ctx", ALL_MODES, indirect=True)
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
 def test_graph_replays_equal_eager(torch_cuda, mode_ctx):
     torch, ctx = torch_cuda, mode_ctx
     H, I, L, m = 512, 1024, 4, 16
@@ -288,7 +283,7 @@ def workspace_views(ws, m, H, I, L):
     return C, acts
 
 
-@pytest.mark.parametrize("mode_ctx", ALL_MODES, indirect=True)
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
 @pytest.mark.parametrize("m", [16, 24, 32])
 def test_full_size_phases_against_oracle(torch_cuda, mode_ctx, oracle_mod, m):
     """Two full-size layers (H = 5120, I = 17408). For the last layer, every
@@ -358,18 +353,17 @@ def run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed, sample):
     return trace
 
 
-@pytest.mark.parametrize("mode_ctx", CUT_MODES, indirect=True)
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
 @pytest.mark.parametrize("shape", [(256, 512, 3), (2048, 8192, 2), (1040, 2064, 2), (3072, 5120, 2)],
                          ids=["tiny", "split-pieces", "ragged", "leftover-units"])
 @pytest.mark.parametrize("m", [1, 8, 16, 17, 32])
 def test_cut_pass_against_oracle(torch_cuda, mode_ctx, oracle_mod, shape, m):
-    """Flow and stream schedules: the last layer's GEMMs (every row) against the
-    oracle and its glue bitwise. "tiny" leaves most work-groups without work,
+    """Both schedules: the last layer's GEMMs (every row) against the oracle and
+    its glue bitwise. "tiny" leaves most work-groups without work,
     "split-pieces" spreads row blocks over several work-groups (partial sums in
     k order), "ragged" has row tiles and k-tiles that do not fill a row block
-    or a k-tile, "leftover-units" gives the stream schedule row groups whose
-    row count is not a multiple of four units. The same pass again is bitwise
-    identical."""
+    or a k-tile, "leftover-units" has row counts that are not a multiple of
+    four row tiles. The same pass again is bitwise identical."""
     torch, ctx = torch_cuda, mode_ctx
     H, I, L = shape
     log("pass mode %d H=%d I=%d L=%d M=%d" % (ctx.get_pass_mode(), H, I, L, m))
@@ -388,7 +382,7 @@ def test_ragged_k_pass_against_oracle(torch_cuda, mode_ctx, oracle_mod):
         run_and_check_last_layer(torch, ctx, oracle_mod, m, 1040, 2064, 2, seed=6, sample=None)
 
 
-@pytest.mark.parametrize("mode_ctx", CUT_MODES, indirect=True)
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
 @pytest.mark.parametrize("m", [16, 32])
 def test_cut_pass_longer_than_one_launch(torch_cuda, mode_ctx, oracle_mod, m):
     """40 layers: two persistent launches (32 + 8 layers); the last layer is
@@ -400,10 +394,10 @@ def test_cut_pass_longer_than_one_launch(torch_cuda, mode_ctx, oracle_mod, m):
     assert torch.isfinite(t1.float()).all()
 
 
-@pytest.mark.parametrize("mode_ctx", CUT_MODES, indirect=True)
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
 def test_cut_pass_large_m_falls_back(torch_cuda, mode_ctx):
-    """M > 32 in the flow and stream modes runs the chained launches: bitwise
-    the composition."""
+    """M > 32 in the persistent mode runs the chained launches: bitwise the
+    composition."""
     torch, ctx = torch_cuda, mode_ctx
     H, I, L, m = 256, 512, 2, 40
     packed, arr = small_stack(torch, ctx, L, H, I)
@@ -415,7 +409,7 @@ def test_cut_pass_large_m_falls_back(torch_cuda, mode_ctx):
     assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16))
 
 
-@pytest.mark.parametrize("mode_ctx", ALL_MODES, indirect=True)
+@pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
 def test_full_stack_stays_finite_and_bounded(torch_cuda, mode_ctx):
     """64 layers at full size, M = 16: the linear glue keeps the RMS O(1)."""
     torch, ctx = torch_cuda, mode_ctx
