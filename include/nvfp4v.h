@@ -369,7 +369,10 @@ int nvfp4v_get_pass_mode(const nvfp4v_ctx *ctx);
  * nvfp4v_pass_status reports; the outputs are then undefined. After the call returns, the
  * workspace holds the last layer's fp32 GEMM outputs (qkv [M][3H] at offset 0,
  * then o [M][H], gu [M][2I] with gate columns 0..I-1 and up columns I..2I-1,
- * d [M][H], each 256-byte aligned).
+ * d [M][H], each 256-byte aligned). For M > 64 the workspace is one such
+ * region per block of 64 rows, in row order: block b (rows 64 b ..) starts at
+ * b * nvfp4v_pass_workspace_bytes(64, hidden, inter, n_layers) and holds its
+ * own rows only.
  * Does not allocate or synchronise. Calls on one context must not overlap.
  * Errors: INVALID_ARG, SHAPE (H or I not a multiple of 16), M_RANGE, ALIGN,
  * WORKSPACE, HIP, FAULT. */

@@ -111,7 +111,7 @@ def test_pass_equals_composition(torch_cuda, mode_ctx, m):
     torch, ctx = torch_cuda, mode_ctx
     H, I, L = 256, 512, 3
     packed, arr = small_stack(torch, ctx, L, H, I)
-    h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=3).view(np.int16)).cuda().view(torch.bfloat16)
+    h0 = torch.from_numpy(synth.activations_bf16(128, H, seed=3).view(np.int16)).cuda().view(torch.bfloat16)
     ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
     h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
     trace = torch.empty((L, m, H), dtype=torch.bfloat16, device="cuda")
@@ -122,17 +122,17 @@ def test_pass_equals_composition(torch_cuda, mode_ctx, m):
     for l in range(L):
         assert torch.equal(trace[l].view(torch.int16), ref[l].view(torch.int16)), "layer %d" % l
     assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16))
-    # the workspace holds the last layer's fp32 outputs; gu in natural [gate | up] order
-    off = 0
-    sizes = [m * 3 * H * 4, m * H * 4, m * 2 * I * 4, m * H * 4]
-    outs = []
-    for sz in sizes:
-        outs.append(ws[off:off + sz].view(torch.float32))
-        off += (sz + 255) // 256 * 256
+    # the workspace holds the last layer's fp32 outputs, q|k|v first, in one
+    # region per block of 64 rows (each the size of a 64-row pass workspace)
     last = packed[-1]
     h_prev = ref[-2] if L > 1 else h0[:m]
     qkv = ctx.verify_gemm(h_prev, last["qkv"], 3 * H, H)
-    assert torch.equal(outs[0].view(m, 3 * H), qkv)
+    region = nv.pass_workspace_bytes(64, H, I, L)
+    for r0 in range(0, m, 64):
+        mc = min(64, m - r0)
+        base = (r0 // 64) * region
+        got = ws[base:base + mc * 3 * H * 4].view(torch.float32).view(mc, 3 * H)
+        assert torch.equal(got, qkv[r0:r0 + mc]), "rows %d.." % r0
 
 
 @pytest.mark.parametrize("plan", ["n:r=1,ks=2", "n:r=2,ks=1"])
