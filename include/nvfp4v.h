@@ -185,6 +185,23 @@ int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_
                        const void *packed_dev, int64_t n, float ts, float *c_dev,
                        hipStream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): nvfp4v_verify_gemm without a
+ * context, on the current HIP device. It allocates nothing: its scratch (the
+ * packed activations of one block of 64 rows, split-K partial sums and arrival
+ * counters) is one file-scope device array of 16 MiB + 64 KiB that every GPU
+ * the library runs on holds until the process ends. Limits: K such that a
+ * block of 64 rows of packed activations fits 8 MiB (K <= 65536), and plans
+ * whose split-K partials fit 8 MiB and use at most 4096 row blocks, else
+ * WORKSPACE. It uses the built-in tile table and exchanges split-K partials
+ * through memory; C equals nvfp4v_verify_gemm's bitwise. Every call on a GPU
+ * shares that GPU's array (a small kernel clears its counters at the start of
+ * each call): calls that overlap on one GPU (other streams, other threads)
+ * race and must not be made. Errors: INVALID_ARG, SHAPE, M_RANGE, ALIGN,
+ * WORKSPACE, HIP, FAULT. */
+int nvfp4v_verify_gemm_static(const uint16_t *a_dev, int64_t m, int64_t k, const void *packed_dev,
+                              int64_t n, float ts, float *c_dev, hipStream_t stream);
+
 /* Activations pre-packed in the GEMM's MFMA fragment order, for callers that
  * produce the next GEMM's input themselves (the chained pass writes them from
  * its glue kernels). nvfp4v_verify_gemm does this packing internally, into the

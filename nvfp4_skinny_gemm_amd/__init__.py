@@ -75,6 +75,7 @@ def load():
     lib.nvfp4v_act_packed_bytes.restype = c.c_size_t
     lib.nvfp4v_pack_activations.argtypes = [p, p, i64, i64, p, p]
     lib.nvfp4v_verify_gemm_pa.argtypes = [p, p, i64, i64, p, i64, c.c_float, p, p]
+    lib.nvfp4v_verify_gemm_static.argtypes = [p, i64, i64, p, i64, c.c_float, p, p]
     lib.nvfp4v_describe_plan.argtypes = [p, i64, i64, i64, c.c_char_p, c.c_size_t]
     lib.nvfp4v_staircase.argtypes = [p, i64, i64, c.c_int, c.c_int, c.c_int, c.c_int,
                                      c.c_size_t, p]
@@ -234,6 +235,24 @@ def fp8_pack_host(codes, row_scales):
     out = np.empty(nb, np.uint8)
     _check(load().nvfp4v_fp8_pack_host(_np_ptr(codes), _np_ptr(row_scales), n, k, _np_ptr(out)),
            "nvfp4v_fp8_pack_host")
+    return out
+
+
+def verify_gemm_static(a, packed, n: int, k: int, ts: float = 1.0, out=None, stream=None):
+    """nvfp4v_verify_gemm_static: the verify GEMM without a context, for callers
+    that cannot allocate (its scratch is a fixed device array of the library;
+    calls must not overlap on one GPU). ``out`` must be given by callers that
+    cannot allocate; without it a tensor is allocated here for convenience."""
+    import torch
+
+    m = a.shape[0]
+    _require(a, "a", _bf16_types(), shape=(m, k))
+    _require(packed, "packed", min_bytes=packed_bytes(n, k))
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=a.device)
+    _require(out, "out", _f32(), shape=(m, n))
+    _check(load().nvfp4v_verify_gemm_static(_t_ptr(a), m, k, _t_ptr(packed), n, float(ts), _t_ptr(out),
+                                            _stream_handle(stream)), "nvfp4v_verify_gemm_static")
     return out
 
 
