@@ -32,6 +32,9 @@ sys.path.insert(0, ROOT)
 H, I, LAYERS = 5120, 17408, 64
 BYTES_PER_WEIGHT = 0.5625  # 4-bit code + one E4M3 byte per 16 weights
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
+CLOCK_GHZ, SIMDS = 2.4, 1024  # 256 CUs x 4 SIMDs
+VALU_CYCLES = 4  # a wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles
 METRIC = "verify-pass µs and achieved HBM GB/s vs M (1..32), full 27B layer stack"
 # Pass schedules (nvfp4v_set_pass_mode) by name.
 SCHEDULES = {"chain": "PASS_CHAIN", "persistent": "PASS_PERSISTENT"}
@@ -157,7 +160,9 @@ def gemm_event_timing(torch, ctx, packed, m, reps=2):
         ms = sum(e0.elapsed_time(e1) for e0, e1, _ in events[name])
         cnt = sum(c for _, _, c in events[name])
         b = int(n * k * BYTES_PER_WEIGHT)
+        flops = 2.0 * 16 * ((m + 15) // 16) * n * k  # the MFMAs run on M padded to 16-row blocks
         per_shape[name] = {"us": round(1e3 * ms / cnt, 2), "GBps": round(b * cnt / (ms * 1e-3) / 1e9, 1),
+                           "mfma_TFLOPs": round(flops * cnt / (ms * 1e-3) / 1e12, 1),
                            "plan": ctx.describe_plan(n, k, m)}
         total_bytes += b * cnt
         total_ms += ms
@@ -246,28 +251,48 @@ def kernel_source_hash():
     """sha256 over the verify GEMM's device sources (the traffic figure in
     profiles/ is valid only for the kernel it was taken on)."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm_device.h"):
-        h.update(open(os.path.join(ROOT, "nvfp4_skinny_gemm_amd", "csrc", f), "rb").read())
+    for f in ("csrc/gemm.hip", "csrc/gemm_device.h", "tables/gfx950.txt"):
+        h.update(open(os.path.join(ROOT, "nvfp4_skinny_gemm_amd", f), "rb").read())
     return h.hexdigest()
 
 
-def traffic_from_profile(gemm_src_hash):
-    """HBM bytes per GEMM launch from the committed rocprofv3 PMC summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "verify_gemm_pmc_fullpass_m16.txt")
+def profile_keys(name, gemm_src_hash):
+    """The `key: value` lines of a committed rocprofv3 summary under profiles/,
+    if it was taken on the current kernel source (same hash); else {}."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
-        return None
+        return {}
     vals = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha256") != gemm_src_hash:
-        return None
+        return {}
+    return vals
+
+
+def traffic_from_profile(gemm_src_hash):
+    """HBM bytes per GEMM launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source; else None."""
     try:
-        return float(vals["traffic_bytes_per_launch"])
+        return float(profile_keys("verify_gemm_pmc_fullpass_m16.txt", gemm_src_hash)["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def utilisation(gemm_src_hash, avg_launch_us):
+    """MFMA and VALU utilisation of the verify GEMM launches: the committed
+    rocprofv3 counters per launch (MFMA busy cycles, VALU instructions), if they
+    were taken on the current kernel source, over the SIMD cycles of this run's
+    average launch (1024 SIMDs at 2.4 GHz); None otherwise."""
+    vals = profile_keys("verify_gemm_pmc_util_m16.txt", gemm_src_hash)
+    simd_cycles = avg_launch_us * 1e-6 * CLOCK_GHZ * 1e9 * SIMDS
+    try:
+        return (float(vals["mfma_busy_cycles_per_launch"]) / simd_cycles,
+                float(vals["valu_insts_per_launch"]) * VALU_CYCLES / simd_cycles)
+    except (KeyError, ValueError):
+        return None, None
 
 
 def parse_sweep(s):
@@ -302,17 +327,85 @@ def find_steps(us, m0=1, persist=2):
     return steps
 
 
+STAIR_SHAPES = (("head", 151936, 5120), ("qkvo", 5120, 5120), ("gate_up", 17408, 5120), ("down", 5120, 17408))
+STAIR_WARMUP, STAIR_ROUNDS = 2, 5  # the library times STAIR_ROUNDS batches of reps launches per M
+
+
 def staircase_report(ctx, m_hi=64, reps=7):
     """A10: microseconds per M (1..m_hi) of the verify GEMM on the LM head and
     the layer shapes (rotating >= 2 GiB of weight copies), with step positions."""
-    shapes = (("head", 151936, 5120), ("qkvo", 5120, 5120), ("gate_up", 17408, 5120), ("down", 5120, 17408))
     out = {}
-    for name, n, k in shapes:
-        us = [round(float(x), 2) for x in ctx.staircase(n, k, 1, m_hi, warmup=2, reps=reps, rotate_bytes=2 << 30)]
+    for name, n, k in STAIR_SHAPES:
+        us = [round(float(x), 2) for x in ctx.staircase(n, k, 1, m_hi, warmup=STAIR_WARMUP, reps=reps,
+                                                         rotate_bytes=2 << 30)]
         out[name] = {"shape": [n, k], "us": us, "steps": find_steps(us),
-                     "GBps_m16": round(n * k * BYTES_PER_WEIGHT / (us[15] * 1e-6) / 1e9, 1)}
-        log("staircase %s [%dx%d]: M1 %.1f us, M16 %.1f, M32 %.1f, M64 %.1f; steps at %s" % (
-            name, n, k, us[0], us[15], us[31], us[63], out[name]["steps"]))
+                     "GBps_m16": round(n * k * BYTES_PER_WEIGHT / (us[15] * 1e-6) / 1e9, 1) if m_hi >= 16 else None}
+        at = lambda m: us[m - 1] if m <= m_hi else float("nan")
+        log("staircase %s [%dx%d]: M1 %.1f us, M16 %.1f, M32 %.1f, M64 %.1f, M128 %.1f; steps at %s" % (
+            name, n, k, at(1), at(16), at(32), at(64), at(128), out[name]["steps"]))
+    return out
+
+
+def summarize_staircase_trace(csv_path, m_hi=64, reps=7):
+    """Per-M kernel durations of a `--staircase-only` run from its rocprofv3
+    kernel trace (CSV): dispatches in start order; each shape's sweep begins
+    with its fill kernel, each M with its activation-packing kernel, followed by
+    STAIR_WARMUP + STAIR_ROUNDS * reps GEMM launches, of which the timed ones
+    are kept. Returns {shape: {"us": [median per M], "steps": [...]}}."""
+    import csv
+    import re
+    import statistics
+
+    rows = list(csv.DictReader(open(csv_path)))
+    col = lambda key: next(c for c in rows[0] if key in c)
+    kn, ks, ke = col("Kernel_Name"), col("Start_Timestamp"), col("End_Timestamp")
+    rows.sort(key=lambda r: int(r[ks]))
+    sections, cur, group = [], None, None
+    for r in rows:
+        found = re.search(r"\b(k_\w+)", r[kn])  # "void (anonymous namespace)::k_gemm<1, 2, 2>(...)"
+        name = found.group(1) if found else r[kn]
+        if name.startswith("k_fill_packed"):
+            cur = []
+            sections.append(cur)
+        elif cur is not None and name.startswith("k_pack_act"):
+            group = []
+            cur.append(group)
+        elif group is not None and name.startswith("k_gemm"):
+            group.append((int(r[ke]) - int(r[ks])) * 1e-3)
+    assert len(sections) == len(STAIR_SHAPES), "expected %d sweeps, found %d" % (len(STAIR_SHAPES), len(sections))
+    out = {}
+    timed = STAIR_ROUNDS * reps
+    for (name, n, k), groups in zip(STAIR_SHAPES, sections):
+        assert len(groups) == m_hi, "%s: %d row counts in the trace" % (name, len(groups))
+        us = []
+        for g in groups:
+            assert len(g) == STAIR_WARMUP + timed, "%s: %d GEMM launches for one M" % (name, len(g))
+            us.append(round(statistics.median(g[STAIR_WARMUP:]), 2))
+        out[name] = {"shape": [n, k], "us": us, "steps": find_steps(us)}
+    return out
+
+
+def summarize_counters(csv_paths):
+    """No GPU: per-kernel mean / min / max of every counter in rocprofv3
+    counter-collection CSVs (one row per dispatch and counter), and the
+    dispatch-weighted mean over all verify GEMM dispatches (k_gemm*)."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    per = defaultdict(list)
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            found = re.search(r"\b(k_\w+(<[^>]*>)?)", r["Kernel_Name"])
+            per[(found.group(1) if found else r["Kernel_Name"][:40], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    out = {}
+    for (kernel, counter), v in sorted(per.items()):
+        out.setdefault(kernel, {})[counter] = {"n": len(v), "mean": sum(v) / len(v), "min": min(v), "max": max(v)}
+    gemm = defaultdict(list)
+    for (kernel, counter), v in per.items():
+        if kernel.startswith("k_gemm"):
+            gemm[counter].extend(v)
+    out["all verify GEMM dispatches"] = {c: {"n": len(v), "mean": sum(v) / len(v)} for c, v in sorted(gemm.items())}
     return out
 
 
@@ -356,13 +449,20 @@ def main():
                     help="pass schedule of the headline number")
     ap.add_argument("--compare", default="persistent",
                     help="comma-separated schedules timed beside the headline one ('' = none)")
-    ap.add_argument("--sweep", default="1-32", help="M values for the per-M pass staircase ('' = none)")
+    ap.add_argument("--sweep", default="1-32,40,48,64,65,96,128", help="M values for the per-M pass staircase ('' = none)")
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-staircase", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip the FP8 output head timing")
     ap.add_argument("--head-only", action="store_true", help="time only the FP8 output head")
+    ap.add_argument("--staircase-only", action="store_true",
+                    help="time only the per-shape staircase (M = 1..--stair-max) and print it as JSON")
+    ap.add_argument("--stair-max", type=int, default=128)
+    ap.add_argument("--summarize-staircase-trace", metavar="CSV",
+                    help="no GPU: per-M kernel durations from the rocprofv3 kernel trace of a --staircase-only run")
+    ap.add_argument("--summarize-counters", metavar="CSV", nargs="+",
+                    help="no GPU: per-kernel counter means from rocprofv3 counter-collection CSVs")
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the verify-GEMM roofline leg and a 256 MiB copy (for hardware-counter runs)")
     args = ap.parse_args()
@@ -371,6 +471,13 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (sharding is "
               "described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1), flush=True)
+        return
+    if args.summarize_staircase_trace:
+        assert args.stair_max <= 64, "the trace summary reads one packing kernel per M (M <= 64)"
+        print(json.dumps(summarize_staircase_trace(args.summarize_staircase_trace, args.stair_max)), flush=True)
+        return
 
     import torch
 
@@ -383,6 +490,11 @@ def main():
     log("device: %s, %d layers" % (torch.cuda.get_device_name(0), layers))
     if args.head_only:
         print(json.dumps({"fp8_head": fp8_head_report(torch, nv, synth, ctx)}), flush=True)
+        ctx.close()
+        return
+    if args.staircase_only:
+        print(json.dumps({"staircase": staircase_report(ctx, m_hi=args.stair_max)}), flush=True)
+        check_device(ctx, nv, "staircase")
         ctx.close()
         return
     packed = build_stack(torch, nv, synth, ctx, layers)
@@ -405,10 +517,12 @@ def main():
     for l, mats in enumerate(packed):
         layer_arr[l] = nv.Layer(mats["qkv"].data_ptr(), mats["o"].data_ptr(),
                                 mats["gate_up"].data_ptr(), mats["down"].data_ptr(), 1.0, 1.0, 1.0, 1.0)
-    h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=0, stream="pass/h0").view("int16")).cuda()
+    rows = max([args.m] + parse_sweep(args.sweep))  # every timed pass reads its first M rows
+    assert 1 <= rows <= nv.MAX_M, "M up to %d" % nv.MAX_M
+    h0 = torch.from_numpy(synth.activations_bf16(rows, H, seed=0, stream="pass/h0").view("int16")).cuda()
     h0 = h0.view(torch.bfloat16)
-    ws = torch.empty(nv.pass_workspace_bytes(64, H, I, layers), dtype=torch.uint8, device="cuda")
-    h_out = torch.empty((64, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(nv.pass_workspace_bytes(rows, H, I, layers), dtype=torch.uint8, device="cuda")
+    h_out = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
     pass_bytes = layer_weight_bytes() * layers
     modes = {name: getattr(nv, const) for name, const in SCHEDULES.items()}
     others = [o for o in args.compare.split(",") if o and o != args.mode]
@@ -459,18 +573,25 @@ def main():
     gbytes, gms, launches, per_shape = gemm_event_timing(torch, ctx, packed, args.m)
     check_device(ctx, nv, "roofline GEMMs")
     achieved = gbytes / (gms * 1e-3) / 1e9
-    traffic = traffic_from_profile(kernel_source_hash())
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile(src_hash)
+    avg_us = gms * 1e3 / launches
+    mfma_util, valu_util = utilisation(src_hash, avg_us)
+    mfma_tflops = sum(v["mfma_TFLOPs"] * v["us"] for v in per_shape.values()) / sum(v["us"] for v in per_shape.values())
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "mfma_util": None if mfma_util is None else round(mfma_util, 4),
+                "valu_util": None if valu_util is None else round(valu_util, 4),
+                "mfma_flops_frac": round(mfma_tflops / PEAK_BF16_TFLOPS, 4),
                 "kernel": "verify GEMM (k_gemm / k_gemm_lds as the tile table picks) at M=%d over the pass's four projection shapes" % args.m,
-                "avg_launch_us": round(gms * 1e3 / launches, 2),
+                "avg_launch_us": round(avg_us, 2),
                 "algorithmic_bytes_per_launch": round(gbytes / launches), "launches": launches,
                 "per_shape": per_shape}
     ceiling = read_ceiling(torch, ctx)
     log("GEMM kernel alone: %.1f GB/s (%.1f%% of peak); read ceiling %.1f GB/s" % (
         achieved, 100 * achieved / PEAK_HBM_GBS, ceiling))
 
-    stair = None if args.no_staircase else staircase_report(ctx)
+    stair = None if args.no_staircase else staircase_report(ctx, m_hi=args.stair_max)
     check_device(ctx, nv, "staircase")
     head = None if args.no_head else fp8_head_report(torch, nv, synth, ctx)
     check_device(ctx, nv, "fp8 head")

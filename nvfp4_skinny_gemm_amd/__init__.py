@@ -13,7 +13,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libnvfp4v.so")
+# NVFP4V_LIBRARY names another build of the same library (the host-sanitizer
+# builds of build.py --sanitize); by default the in-tree libnvfp4v.so.
+LIB_PATH = os.environ.get("NVFP4V_LIBRARY") or os.path.join(HERE, "libnvfp4v.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "nvfp4v.h")
 
 OK = 0

@@ -29,9 +29,20 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-I", OBJ, "-c", os.path.join(CSRC, src), "-o", obj]
+def _host_sanitizer_flags(sanitize: str) -> list:
+    """Host-only sanitizer flags: each applies to the host pass alone (the GPU
+    code is built as usual)."""
+    flags = []
+    for f in ("-fsanitize=" + sanitize, "-fno-sanitize-recover=all", "-g", "-fno-omit-frame-pointer"):
+        flags += ["-Xarch_host", f]
+    return flags
+
+
+def _compile(src: str, sanitize: str = "") -> str:
+    odir = os.path.join(OBJ, sanitize) if sanitize else OBJ
+    obj = os.path.join(odir, os.path.splitext(src)[0] + ".o")
+    extra = _host_sanitizer_flags(sanitize) if sanitize else []
+    cmd = [HIPCC, *CFLAGS, *extra, "-I", OBJ, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
@@ -53,22 +64,33 @@ def _embed_table() -> None:
             f.write(body)
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, sanitize: str = "") -> str:
+    """Build libnvfp4v.so. With `sanitize` ("address", "undefined" or "thread")
+    the host code is instrumented and the library goes to
+    _build/<sanitize>/libnvfp4v.so instead (load it with NVFP4V_LIBRARY and the
+    matching clang runtime in LD_PRELOAD; for CPU-only runs)."""
+    assert sanitize in ("", "address", "undefined", "thread"), sanitize
+    os.makedirs(os.path.join(OBJ, sanitize) if sanitize else OBJ, exist_ok=True)
     _embed_table()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, sanitize), SOURCES))
+    lib = os.path.join(OBJ, sanitize, "libnvfp4v.so") if sanitize else LIB
+    tmp = lib + ".tmp"
+    link = ["-Xarch_host", "-fsanitize=" + sanitize] if sanitize else []
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import argparse
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--sanitize", default="", choices=("", "address", "undefined", "thread"))
+    build(verbose=True, sanitize=ap.parse_args().sanitize)
     sys.exit(0)

@@ -23,7 +23,12 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.cpp")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZE=address|thread|undefined selects a build of the oracle with
+# that g++ sanitizer (run with the matching runtime in LD_PRELOAD, e.g.
+# LD_PRELOAD=$(g++ -print-file-name=libasan.so)).
+_SANITIZE = os.environ.get("ORACLE_SANITIZE", "")
+assert _SANITIZE in ("", "address", "thread", "undefined"), "ORACLE_SANITIZE=%r" % _SANITIZE
+_LIB = os.path.join(_HERE, "liboracle%s.so" % ("_" + _SANITIZE if _SANITIZE else ""))
 
 _lib = None
 
@@ -34,6 +39,8 @@ def build(force: bool = False) -> str:
         tmp = _LIB + ".tmp"
         cmd = ["g++", "-std=c++17", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
                "-shared", "-pthread", _SRC, "-o", tmp]
+        if _SANITIZE:
+            cmd[1:1] = ["-fsanitize=" + _SANITIZE, "-fno-sanitize-recover=all", "-g", "-fno-omit-frame-pointer"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
