@@ -409,6 +409,65 @@ def summarize_counters(csv_paths):
     return out
 
 
+def attention_report(torch, nv, synth, ctx, ctxs=(1024, 4096, 16384, 32768), ms=(1, 8, 16, 17, 24, 32),
+                     hq=40, hkv=40, warmup=3, reps=20):
+    """Tree-verify attention of one layer (40 heads of 128, the stand-in layer's
+    q, k and v) per context length and tree size: microseconds per call and the
+    key/value bytes read per second. Random bf16 caches, rotated over enough
+    copies (>= 512 MiB) that every call streams them from HBM. The `reps` calls
+    are captured in a HIP graph and replayed, so the figure is the kernel's
+    time, not the Python binding's per-call overhead."""
+    d = 128
+    out = {"heads": [hq, hkv], "head_dim": d, "us": {}, "GBps": {}, "plan": {}}
+    for T in ctxs:
+        cap = (T + max(ms) + 31) // 32 * 32
+        nbytes = nv.kv_cache_bytes(cap, hkv, d)
+        copies = max(1, min(24, -(-(512 << 20) // (2 * nbytes))))
+        caches = []
+        g = torch.Generator(device="cuda")
+        g.manual_seed(T)
+        for _ in range(copies):
+            kc = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            vc = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            rows = torch.randn((cap, hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+            ctx.kv_write(rows, rows.roll(1, 0).contiguous(), 0, cap, kc, vc)
+            caches.append((kc, vc))
+            del rows
+        for m in ms:
+            q = torch.randn((m, hq, d), generator=g, device="cuda").to(torch.bfloat16)
+            parent = synth.tree_parent_rows(m, seed=m)
+            ws = torch.zeros(nv.tree_attention_workspace_bytes(T, m, hq, hkv, d), dtype=torch.uint8, device="cuda")
+            o = torch.empty((m, hq, d), dtype=torch.float32, device="cuda")
+            for i in range(warmup):
+                kc, vc = caches[i % copies]
+                ctx.tree_attention(q, kc, vc, cap, T, hkv, parent, out=o, ws=ws)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(reps):
+                    kc, vc = caches[i % copies]
+                    ctx.tree_attention(q, kc, vc, cap, T, hkv, parent, out=o, ws=ws)
+            graph.replay()  # warm
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(2):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            del graph
+            us = e0.elapsed_time(e1) * 1e3 / (2 * reps)
+            key = "%d/%d" % (T, m)
+            out["us"][key] = round(us, 2)
+            out["GBps"][key] = round((T + m) * hkv * d * 4 / (us * 1e-6) / 1e9, 1)
+            out["plan"][key] = list(ctx.tree_attention_plan(T, m, hq, hkv, d))
+        log("tree attention, %d heads, context %d: %s us; %s GB/s" % (
+            hq, T, [out["us"]["%d/%d" % (T, m)] for m in ms], [out["GBps"]["%d/%d" % (T, m)] for m in ms]))
+        del caches
+        torch.cuda.empty_cache()
+    return out
+
+
 def fp8_head_report(torch, nv, synth, ctx, ms=(1, 8, 16, 24, 32), warmup=3, reps=20):
     """The FP8 output head (151936 x 5120 E4M3 codes + fp32 row scales, the
     step after the last layer): microseconds per launch and weight GB/s at the
@@ -456,6 +515,8 @@ def main():
     ap.add_argument("--no-staircase", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip the FP8 output head timing")
     ap.add_argument("--head-only", action="store_true", help="time only the FP8 output head")
+    ap.add_argument("--no-attention", action="store_true", help="skip the tree-verify attention timing")
+    ap.add_argument("--attention-only", action="store_true", help="time only the tree-verify attention")
     ap.add_argument("--staircase-only", action="store_true",
                     help="time only the per-shape staircase (M = 1..--stair-max) and print it as JSON")
     ap.add_argument("--stair-max", type=int, default=128)
@@ -490,6 +551,10 @@ def main():
     log("device: %s, %d layers" % (torch.cuda.get_device_name(0), layers))
     if args.head_only:
         print(json.dumps({"fp8_head": fp8_head_report(torch, nv, synth, ctx)}), flush=True)
+        ctx.close()
+        return
+    if args.attention_only:
+        print(json.dumps({"tree_attention": attention_report(torch, nv, synth, ctx)}), flush=True)
         ctx.close()
         return
     if args.staircase_only:
@@ -595,6 +660,7 @@ def main():
     check_device(ctx, nv, "staircase")
     head = None if args.no_head else fp8_head_report(torch, nv, synth, ctx)
     check_device(ctx, nv, "fp8 head")
+    attn = None if args.no_attention else attention_report(torch, nv, synth, ctx)
 
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
@@ -613,6 +679,7 @@ def main():
         "read_ceiling_GBps": round(ceiling, 1),
         "staircase": stair,
         "fp8_head": head,
+        "tree_attention": attn,
         "pages_context": PAGES_CONTEXT,
     }
     # Release every device object (weights, workspace, the context) before the

@@ -202,6 +202,65 @@ int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_
 int nvfp4v_verify_gemm_static(const uint16_t *a_dev, int64_t m, int64_t k, const void *packed_dev,
                               int64_t n, float ts, float *c_dev, hipStream_t stream);
 
+/* ---- Tree-verify attention ------------------------------------------------
+ * One attention layer of the verify pass for the M rows of one draft tree
+ * (row 0 the root token, then the tree's nodes, parents before children)
+ * against the committed context (the served model mixes Gated DeltaNet layers
+ * with attention layers: TandemLLM manual, "What TandemLLM is", 1.1 "The test
+ * environment"; every row of the tree goes through each layer in one pass:
+ * 1.2 "Two levers"; the cost is measured per context length from 1k to 32k:
+ * release post, the paragraph on what checking 8 to 32 guesses costs):
+ *     O[i][h] = sum_j softmax_j(scale * q[i][h] . k[j][h / G]) v[j][h / G]
+ * over the positions j row i sees: every context position 0..T-1 and the tree
+ * rows on its own path to the root, itself included, whose keys and values
+ * are at cache positions T + row. G = Hq / Hkv query heads share a key/value
+ * head. bf16 inputs, fp32 arithmetic (the softmax weights enter the value
+ * product as two bf16 terms), fp32 output; bitwise reproducible.
+ *
+ * Caches (device, caller-owned, nvfp4v_kv_cache_bytes(cap, Hkv, D) bytes each):
+ * an opaque MFMA-fragment order of keys and values for positions 0..cap-1
+ * (cap a multiple of 32), written by nvfp4v_kv_write. Head dim D = 128. */
+#define NVFP4V_ATTN_HEAD_DIM 128
+#define NVFP4V_ATTN_MAX_ROWS 32 /* G * M <= 32 query columns per key/value head */
+size_t nvfp4v_kv_cache_bytes(int64_t cap, int hkv, int d); /* 0 for a bad shape */
+
+/* Write n rows of keys and values, bf16 [n][Hkv][D] row-major each, to cache
+ * positions pos0 .. pos0 + n - 1 (a device kernel on `stream`; does not
+ * allocate or synchronise). Errors: INVALID_ARG, SHAPE (D != 128, Hkv not in
+ * 1..64, cap not a positive multiple of 32, positions beyond cap), ALIGN, HIP,
+ * FAULT. */
+int nvfp4v_kv_write(nvfp4v_ctx *ctx, const uint16_t *k_rows_dev, const uint16_t *v_rows_dev, int64_t n,
+                    int64_t pos0, int hkv, int d, int64_t cap, uint16_t *k_cache_dev,
+                    uint16_t *v_cache_dev, hipStream_t stream);
+
+/* Workspace of nvfp4v_tree_attention (0 for a bad shape). Its first 256 bytes
+ * are arrival tickets that must be zero before the first call (hipMemset once);
+ * every call leaves them zero. */
+size_t nvfp4v_tree_attention_workspace_bytes(int64_t ctx_len, int64_t m, int hq, int hkv, int d);
+
+/* Enqueue the attention of M tree rows (1 <= M, (Hq / Hkv) * M <= 32) on
+ * `stream`. q: bf16 [M][Hq][D]; k_cache / v_cache: positions 0..ctx_len-1 the
+ * context, ctx_len + i tree row i (ctx_len + M <= cap); parent_rows: HOST
+ * array of M int32, parent_rows[0] = -1, 0 <= parent_rows[i] < i; scale: the
+ * score scale (1/sqrt(D) for plain attention); o: fp32 [M][Hq][D]. The keys
+ * and values of positions beyond ctx_len + M are never used (any bits there,
+ * NaN included, leave O unchanged). Work: one work-group per (key/value head,
+ * chunk of positions), the last of a head merging the chunks in order. Does
+ * not allocate or synchronise; calls sharing a workspace must not overlap.
+ * Errors: INVALID_ARG (null pointer, bad parent_rows, non-finite scale),
+ * SHAPE, M_RANGE, ALIGN, WORKSPACE, HIP, FAULT. */
+int nvfp4v_tree_attention(nvfp4v_ctx *ctx, const uint16_t *q_dev, const uint16_t *k_cache_dev,
+                          const uint16_t *v_cache_dev, int64_t cap, int64_t ctx_len, int64_t m, int hq,
+                          int hkv, int d, const int32_t *parent_rows, float scale, float *o_dev,
+                          void *ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/* The chunking nvfp4v_tree_attention uses for a shape on the context's GPU
+ * (chunks per key/value head: one resident wave of work-groups over the CUs,
+ * at least 128 positions and at most 64 chunks; positions per chunk), for
+ * reports. Errors: INVALID_ARG, SHAPE, M_RANGE, HIP. */
+int nvfp4v_tree_attention_plan(nvfp4v_ctx *ctx, int64_t ctx_len, int64_t m, int hq, int hkv, int d,
+                               int *nchunks, int *chunk);
+
 /* Activations pre-packed in the GEMM's MFMA fragment order, for callers that
  * produce the next GEMM's input themselves (the chained pass writes them from
  * its glue kernels). nvfp4v_verify_gemm does this packing internally, into the

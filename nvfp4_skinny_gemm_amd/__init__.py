@@ -103,6 +103,14 @@ def load():
     lib.nvfp4v_fp8_head_gemm.argtypes = [p, p, i64, i64, p, i64, p, p]
     lib.nvfp4v_fp8_head_gemm_pa.argtypes = [p, p, i64, i64, p, i64, p, p]
     lib.nvfp4v_staircut.argtypes = [p, c.c_int, p, p, c.c_int, p, c.c_int, p, p, p, p]
+    lib.nvfp4v_kv_cache_bytes.argtypes = [i64, c.c_int, c.c_int]
+    lib.nvfp4v_kv_cache_bytes.restype = c.c_size_t
+    lib.nvfp4v_kv_write.argtypes = [p, p, p, i64, i64, c.c_int, c.c_int, i64, p, p, p]
+    lib.nvfp4v_tree_attention_workspace_bytes.argtypes = [i64, i64, c.c_int, c.c_int, c.c_int]
+    lib.nvfp4v_tree_attention_workspace_bytes.restype = c.c_size_t
+    lib.nvfp4v_tree_attention.argtypes = [p, p, p, p, i64, i64, i64, c.c_int, c.c_int, c.c_int, p,
+                                          c.c_float, p, p, c.c_size_t, p]
+    lib.nvfp4v_tree_attention_plan.argtypes = [p, i64, i64, c.c_int, c.c_int, c.c_int, p, p]
     _lib = lib
     return lib
 
@@ -256,6 +264,19 @@ def verify_gemm_static(a, packed, n: int, k: int, ts: float = 1.0, out=None, str
     _check(load().nvfp4v_verify_gemm_static(_t_ptr(a), m, k, _t_ptr(packed), n, float(ts), _t_ptr(out),
                                             _stream_handle(stream)), "nvfp4v_verify_gemm_static")
     return out
+
+
+ATTN_HEAD_DIM = 128
+ATTN_MAX_ROWS = 32
+
+
+def kv_cache_bytes(cap: int, hkv: int, d: int = ATTN_HEAD_DIM) -> int:
+    """Bytes of one key or value cache of `cap` positions (a multiple of 32)."""
+    return int(load().nvfp4v_kv_cache_bytes(cap, hkv, d))
+
+
+def tree_attention_workspace_bytes(ctx_len: int, m: int, hq: int, hkv: int, d: int = ATTN_HEAD_DIM) -> int:
+    return int(load().nvfp4v_tree_attention_workspace_bytes(ctx_len, m, hq, hkv, d))
 
 
 def staircut(us_by_rows, parent, p_accept, sizes=None):
@@ -431,6 +452,63 @@ class Context:
         _check(load().nvfp4v_fp8_head_gemm_pa(self._h, _t_ptr(act), m, k, _t_ptr(packed), n,
                                               _t_ptr(out), _stream_handle(stream)),
                "nvfp4v_fp8_head_gemm_pa")
+        return out
+
+    # -- tree-verify attention ----------------------------------------------
+    def tree_attention_plan(self, ctx_len: int, m: int, hq: int, hkv: int, d: int = ATTN_HEAD_DIM):
+        """(chunks per key/value head, positions per chunk) of tree_attention on this GPU."""
+        nch, chunk = ctypes.c_int(0), ctypes.c_int(0)
+        _check(load().nvfp4v_tree_attention_plan(self._h, ctx_len, m, hq, hkv, d, ctypes.byref(nch),
+                                                 ctypes.byref(chunk)), "nvfp4v_tree_attention_plan")
+        return nch.value, chunk.value
+
+    def kv_write(self, k_rows, v_rows, pos0: int, cap: int, k_cache, v_cache, stream=None):
+        """Write keys / values bf16 [n, Hkv, 128] to cache positions pos0 .. pos0 + n - 1."""
+        n, hkv, d = k_rows.shape
+        _require(k_rows, "k_rows", _bf16_types(), shape=(n, hkv, d))
+        _require(v_rows, "v_rows", _bf16_types(), shape=(n, hkv, d))
+        nb = kv_cache_bytes(cap, hkv, d)
+        if nb == 0:
+            raise ValueError("bad cache shape: cap=%d (a positive multiple of 32), hkv=%d, d=%d (128)" % (cap, hkv, d))
+        _require(k_cache, "k_cache", min_bytes=nb)
+        _require(v_cache, "v_cache", min_bytes=nb)
+        _check(load().nvfp4v_kv_write(self._h, _t_ptr(k_rows), _t_ptr(v_rows), n, pos0, hkv, d, cap,
+                                      _t_ptr(k_cache), _t_ptr(v_cache), _stream_handle(stream)), "nvfp4v_kv_write")
+
+    def tree_attention(self, q, k_cache, v_cache, cap: int, ctx_len: int, hkv: int, parent_rows,
+                       scale: float = None, out=None, ws=None, stream=None):
+        """O fp32 [M, Hq, 128] of the tree rows q (bf16 [M, Hq, 128]) against the cached
+        context (positions 0..ctx_len-1) and their own root paths (parent_rows: M ints,
+        -1 for row 0). `ws` (uint8, tree_attention_workspace_bytes, its first 256 bytes
+        zero before the first use) is allocated zeroed when not given."""
+        import numpy as np
+        import torch
+
+        m, hq, d = q.shape
+        _require(q, "q", _bf16_types(), shape=(m, hq, d))
+        nb = kv_cache_bytes(cap, hkv, d)
+        if nb == 0:
+            raise ValueError("bad cache shape: cap=%d, hkv=%d, d=%d" % (cap, hkv, d))
+        _require(k_cache, "k_cache", min_bytes=nb)
+        _require(v_cache, "v_cache", min_bytes=nb)
+        par = np.ascontiguousarray(np.asarray(parent_rows, dtype=np.int32))
+        if par.shape != (m,):
+            raise ValueError("parent_rows must hold one entry per tree row")
+        wsb = tree_attention_workspace_bytes(ctx_len, m, hq, hkv, d)
+        if wsb == 0:
+            raise ValueError("bad attention shape: ctx_len=%d m=%d hq=%d hkv=%d d=%d" % (ctx_len, m, hq, hkv, d))
+        if ws is None:
+            ws = torch.zeros(wsb, dtype=torch.uint8, device=q.device)
+        _require(ws, "ws", min_bytes=wsb)
+        if out is None:
+            out = torch.empty((m, hq, d), dtype=torch.float32, device=q.device)
+        _require(out, "out", _f32(), shape=(m, hq, d))
+        if scale is None:
+            scale = 1.0 / float(np.sqrt(d))
+        _check(load().nvfp4v_tree_attention(self._h, _t_ptr(q), _t_ptr(k_cache), _t_ptr(v_cache), cap, ctx_len, m,
+                                            hq, hkv, d, _np_ptr(par), float(scale), _t_ptr(out), _t_ptr(ws),
+                                            ws.numel() * ws.element_size(), _stream_handle(stream)),
+               "nvfp4v_tree_attention")
         return out
 
     # -- chain glue and the full pass ---------------------------------------

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libnvfp4v.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "format.hip", "gemm.hip", "staircase.hip", "pass.hip", "measure.hip", "head.hip", "staircut.cpp", "noalloc.hip"]
+SOURCES = ["api.hip", "format.hip", "gemm.hip", "staircase.hip", "pass.hip", "measure.hip", "head.hip", "staircut.cpp", "noalloc.hip", "attention.hip"]
 
 CFLAGS = [
     "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",

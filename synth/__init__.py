@@ -169,6 +169,27 @@ def draft_tree(n: int, seed: int = 0, stream: str = "tree", shape: str = "random
     return parent, p
 
 
+def attention_inputs(m: int, hq: int, hkv: int, ctx_len: int, d: int = 128, seed: int = 0,
+                     stream: str = "attn"):
+    """Tree-verify attention inputs as bf16 bit patterns: queries [m][hq][d] and
+    keys / values [hkv][ctx_len + m][d] (positions ctx_len + i are tree row
+    i's), all N(0, 1) like the projections' outputs after the linear glue."""
+    g = rng(seed, stream, m, hq, hkv, ctx_len, d)
+    q = _to_bf16_bits(g.standard_normal((m, hq, d), dtype=np.float32))
+    k = _to_bf16_bits(g.standard_normal((hkv, ctx_len + m, d), dtype=np.float32))
+    v = _to_bf16_bits(g.standard_normal((hkv, ctx_len + m, d), dtype=np.float32))
+    return q, k, v
+
+
+def tree_parent_rows(m: int, seed: int = 0, shape: str = "random", stream: str = "attn-tree"):
+    """Parent rows of an m-row verify tree: row 0 is the root (-1), rows 1..m-1
+    the nodes of draft_tree(m - 1) (a node under the root hangs from row 0)."""
+    if m == 1:
+        return np.array([-1], np.int32)
+    parent, _ = draft_tree(m - 1, seed=seed, stream=stream, shape=shape)
+    return np.concatenate([[-1], parent.astype(np.int64) + 1]).astype(np.int32)
+
+
 def staircase_us(max_rows: int = 64, seed: int = 0, stream: str = "stairs", base: float = 3800.0,
                  step_rows: int = 8, step: float = 0.2):
     """A synthetic staircase for the cut: us_by_rows[r - 1], flat within each

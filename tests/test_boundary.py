@@ -293,3 +293,72 @@ def test_pass_modes():
         assert lib.nvfp4v_set_pass_mode(ctx, bad) == nv.E_INVALID_ARG
         assert lib.nvfp4v_get_pass_mode(ctx) == nv.PASS_PERSISTENT
     assert lib.nvfp4v_set_pass_mode(None, nv.PASS_CHAIN) == nv.E_INVALID_ARG
+
+
+@host_only
+def test_tree_attention_host_checks():
+    """Tree-verify attention: shape, range, tree and alignment checks return
+    before anything reaches the GPU."""
+    lib = nv.load()
+    ctx = FakeCtx().ptr
+    dev = fake_dev()
+    par = np.array([-1, 0, 1, 1], np.int32)
+    pp = ctypes.c_void_p(par.ctypes.data)
+
+    def call(m=4, ctx_len=10, hq=2, hkv=2, d=128, parent=pp, scale=0.1, cap=64, q=dev, o=dev, ws=dev):
+        return lib.nvfp4v_tree_attention(ctx, q, dev, dev, cap, ctx_len, m, hq, hkv, d, parent, scale, o, ws,
+                                         1 << 20, None)
+
+    assert lib.nvfp4v_tree_attention(None, dev, dev, dev, 64, 10, 4, 2, 2, 128, pp, 0.1, dev, dev, 1 << 20,
+                                     None) == nv.E_INVALID_ARG
+    assert call(q=None) == nv.E_INVALID_ARG
+    assert call(parent=None) == nv.E_INVALID_ARG
+    assert call(d=64) == nv.E_SHAPE
+    assert call(hq=3) == nv.E_SHAPE
+    assert call(hq=130, hkv=65) == nv.E_SHAPE
+    assert call(ctx_len=61) == nv.E_SHAPE
+    assert call(cap=48) == nv.E_SHAPE
+    assert call(m=0) == nv.E_M_RANGE
+    assert call(m=33) == nv.E_M_RANGE
+    assert call(hq=16, hkv=2, m=5) == nv.E_M_RANGE
+    bad = np.array([-1, 0, 2, 1], np.int32)  # row 2 is its own parent
+    assert call(parent=ctypes.c_void_p(bad.ctypes.data)) == nv.E_INVALID_ARG
+    bad0 = np.array([0, 0, 1, 1], np.int32)
+    assert call(parent=ctypes.c_void_p(bad0.ctypes.data)) == nv.E_INVALID_ARG
+    assert call(scale=float("inf")) == nv.E_INVALID_ARG
+    assert call(o=fake_dev(0x1004)) == nv.E_ALIGN
+
+
+def test_attention_sizes():
+    # caches: cap * Hkv * 128 bf16 each
+    assert nv.kv_cache_bytes(64, 40) == 64 * 40 * 128 * 2
+    assert nv.kv_cache_bytes(48, 40) == 0 and nv.kv_cache_bytes(64, 40, 64) == 0 and nv.kv_cache_bytes(0, 1) == 0
+    # workspace: 256 bytes of tickets + one record per (head, chunk), at most
+    # one chunk per 128 positions and 64 chunks per head
+    one = nv.tree_attention_workspace_bytes(100, 16, 40, 40)
+    rec1 = (16 * 2 + 8 * 64 * 4) * 4  # one 16-column block
+    assert one == 256 + 40 * 1 * rec1
+    assert nv.tree_attention_workspace_bytes(32768, 16, 40, 40) == 256 + 40 * 64 * rec1
+    rec2 = (32 * 2 + 2 * 8 * 64 * 4) * 4
+    assert nv.tree_attention_workspace_bytes(1000, 17, 40, 40) == 256 + 40 * 8 * rec2  # 1017 positions
+    assert nv.tree_attention_workspace_bytes(10, 33, 40, 40) == 0
+    assert nv.tree_attention_workspace_bytes(10, 4, 40, 40, 64) == 0
+
+
+@host_only
+def test_kv_write_host_checks():
+    lib = nv.load()
+    ctx = FakeCtx().ptr
+    dev = fake_dev()
+
+    def call(n=4, pos0=0, hkv=2, d=128, cap=64, k=dev):
+        return lib.nvfp4v_kv_write(ctx, k, dev, n, pos0, hkv, d, cap, dev, dev, None)
+
+    assert lib.nvfp4v_kv_write(None, dev, dev, 4, 0, 2, 128, 64, dev, dev, None) == nv.E_INVALID_ARG
+    assert call(k=None) == nv.E_INVALID_ARG
+    assert call(d=64) == nv.E_SHAPE
+    assert call(hkv=0) == nv.E_SHAPE
+    assert call(cap=40) == nv.E_SHAPE
+    assert call(n=0) == nv.E_SHAPE
+    assert call(pos0=61) == nv.E_SHAPE
+    assert call(k=fake_dev(0x1008)) == nv.E_ALIGN
