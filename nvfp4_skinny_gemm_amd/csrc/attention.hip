@@ -136,29 +136,30 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
     for (int d = 0; d < DBLK; ++d) oacc[cb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Each wave walks its 32-position groups with the next group's keys and
-  // values requested as soon as the current ones have been consumed: the keys
-  // after the S^T products, the values after the P V products.
-  bf16x8 kf[2][KSTEP], vf[DBLK];
-  auto load_k = [&](int pb) {
+  // Each wave walks its 32-position groups (gi = wave, wave + 4, ...) with the
+  // keys and values of later groups requested as soon as a register set has
+  // been consumed: its keys after the S^T products, its values after the P V
+  // products. With one column block the wave keeps two register sets, so two
+  // groups are in flight; with two it keeps one (registers). The groups are
+  // processed in the same order either way.
+  constexpr int SETS = NB == 1 ? 2 : 1;
+  bf16x8 kf[SETS][2][KSTEP], vf[SETS][DBLK];
+  auto pos_of = [&](int gi) { return p0 + gi * GROUP_POS; };
+  auto load_k = [&](int set, int pb) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int s = 0; s < KSTEP; ++s) kf[t][s] = load16(a.kc + kfrag(a, h, pb / 16 + t, s, lane));
+      for (int s = 0; s < KSTEP; ++s) kf[set][t][s] = load16(a.kc + kfrag(a, h, pb / 16 + t, s, lane));
   };
-  auto load_v = [&](int pb) {
+  auto load_v = [&](int set, int pb) {
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d) vf[d] = load16(a.vc + vfrag(a, h, pb / 32, d, lane));
+    for (int d = 0; d < DBLK; ++d) vf[set][d] = load16(a.vc + vfrag(a, h, pb / 32, d, lane));
   };
-  if (wave < ngroups) {
-    load_k(p0 + wave * GROUP_POS);
-    load_v(p0 + wave * GROUP_POS);
-  }
-  for (int gi = wave; gi < ngroups; gi += ATTN_WAVES) {
-    const int pbase = p0 + gi * GROUP_POS;  // a multiple of 32
-    const bool more = gi + ATTN_WAVES < ngroups;
-    const int pnext = pbase + ATTN_WAVES * GROUP_POS;
-
+  // One group with register set `set`; then that set is refilled with group
+  // gnext (if it exists).
+  auto step = [&](int set, int gi, int gnext) {
+    const int pbase = pos_of(gi);  // a multiple of 32
+    const bool more = gnext < ngroups;
     f32x4 st[NB][2];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb)
@@ -167,9 +168,9 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
         st[cb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KSTEP; ++s)
-          st[cb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][s], qf[cb][s], st[cb][t], 0, 0, 0);
+          st[cb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[set][t][s], qf[cb][s], st[cb][t], 0, 0, 0);
       }
-    if (more) load_k(pnext);
+    if (more) load_k(set, pos_of(gnext));
 
     if (pbase + GROUP_POS > a.P) {
       // Cache slots past the last position may hold anything (NaN included):
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
         const int pos = pbase + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
         if (pos >= a.P) {
 #pragma unroll
-          for (int d = 0; d < DBLK; ++d) vf[d][j] = (__bf16)0.f;
+          for (int d = 0; d < DBLK; ++d) vf[set][d][j] = (__bf16)0.f;
         }
       }
     }
@@ -219,11 +220,28 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
 #pragma unroll
       for (int d = 0; d < DBLK; ++d) {
         oacc[cb][d] *= alpha;
-        oacc[cb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], phi, oacc[cb][d], 0, 0, 0);
-        oacc[cb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], plo, oacc[cb][d], 0, 0, 0);
+        oacc[cb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[set][d], phi, oacc[cb][d], 0, 0, 0);
+        oacc[cb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[set][d], plo, oacc[cb][d], 0, 0, 0);
       }
     }
-    if (more) load_v(pnext);
+    if (more) load_v(set, pos_of(gnext));
+  };
+
+  constexpr int STRIDE = ATTN_WAVES * SETS;  // groups between two uses of one register set
+#pragma unroll
+  for (int sset = 0; sset < SETS; ++sset) {
+    const int gi = wave + sset * ATTN_WAVES;
+    if (gi < ngroups) {
+      load_k(sset, pos_of(gi));
+      load_v(sset, pos_of(gi));
+    }
+  }
+  for (int gi = wave; gi < ngroups; gi += STRIDE) {
+#pragma unroll
+    for (int sset = 0; sset < SETS; ++sset) {
+      const int gs = gi + sset * ATTN_WAVES;
+      if (gs < ngroups) step(sset, gs, gs + STRIDE);
+    }
   }
 
   // ---- merge the four waves in LDS (wave order) ----
