@@ -409,7 +409,10 @@ def summarize_counters(csv_paths):
     return out
 
 
-def attention_report(torch, nv, synth, ctx, ctxs=(1024, 4096, 16384, 32768), ms=(1, 8, 16, 17, 24, 32),
+ATTN_CTXS, ATTN_MS = (1024, 4096, 16384, 32768), (1, 8, 16, 17, 24, 32)
+
+
+def attention_report(torch, nv, synth, ctx, ctxs=ATTN_CTXS, ms=ATTN_MS,
                      hq=40, hkv=40, warmup=3, reps=20):
     """Tree-verify attention of one layer (40 heads of 128, the stand-in layer's
     q, k and v) per context length and tree size: microseconds per call and the
@@ -468,6 +471,61 @@ def attention_report(torch, nv, synth, ctx, ctxs=(1024, 4096, 16384, 32768), ms=
     return out
 
 
+def summarize_attention_trace(csv_path, counters=None):
+    """No GPU: per (context, M) kernel durations of an `--attention-only` run
+    from its rocprofv3 kernel trace. Per (context, M), in the order
+    attention_report times them, the tree-attention dispatches come as a run of
+    3 warm-up calls and a run of 60 graph-replayed ones (other kernels, the
+    inputs' generation and the graph capture's own, separate the runs); the
+    median of each 60-dispatch run. With `counters` (counter-collection CSVs of
+    the same command), the per-dispatch means of each counter over those runs."""
+    import csv
+    import re
+    import statistics
+
+    rows = list(csv.DictReader(open(csv_path)))
+    col = lambda key: next(c for c in rows[0] if key in c)
+    kn, ks, ke = col("Kernel_Name"), col("Start_Timestamp"), col("End_Timestamp")
+    rows.sort(key=lambda r: int(r[ks]))
+    runs, cur = [], None
+    for r in rows:
+        if re.search(r"\bk_tree_attn<", r[kn]):
+            if cur is None:
+                cur = []
+                runs.append(cur)
+            cur.append((int(r[ke]) - int(r[ks])) * 1e-3)
+        else:
+            cur = None
+    runs = [r for r in runs if len(r) > 3]
+    keys = ["%d/%d" % (t, m) for t in ATTN_CTXS for m in ATTN_MS]
+    assert len(runs) == len(keys), "expected %d runs of attention dispatches, found %d" % (len(keys), len(runs))
+    out = {"us": {}, "GBps": {}}
+    for key, run in zip(keys, runs):
+        t, m = map(int, key.split("/"))
+        us = statistics.median(run)
+        out["us"][key] = round(us, 2)
+        out["GBps"][key] = round((t + m) * 40 * 128 * 4 / (us * 1e-6) / 1e9, 1)
+    if counters:
+        per = {}
+        for path in counters:
+            cnt_rows = [r for r in csv.DictReader(open(path)) if re.search(r"\bk_tree_attn<", r["Kernel_Name"])]
+            # rocprofv3 numbers dispatches in order; consecutive ids form the runs
+            cnt_rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+            runs_c, prev = [], None
+            for r in cnt_rows:
+                d = int(r["Dispatch_Id"])
+                if prev is None or d != prev + 1:
+                    runs_c.append([])
+                runs_c[-1].append(float(r["Counter_Value"]))
+                prev = d
+            runs_c = [r for r in runs_c if len(r) > 3]
+            assert len(runs_c) == len(keys), "expected %d runs in %s, found %d" % (len(keys), path, len(runs_c))
+            name = cnt_rows[0]["Counter_Name"]
+            per[name] = {k: round(sum(v) / len(v), 1) for k, v in zip(keys, runs_c)}
+        out["counters"] = per
+    return out
+
+
 def fp8_head_report(torch, nv, synth, ctx, ms=(1, 8, 16, 24, 32), warmup=3, reps=20):
     """The FP8 output head (151936 x 5120 E4M3 codes + fp32 row scales, the
     step after the last layer): microseconds per launch and weight GB/s at the
@@ -522,6 +580,9 @@ def main():
     ap.add_argument("--stair-max", type=int, default=128)
     ap.add_argument("--summarize-staircase-trace", metavar="CSV",
                     help="no GPU: per-M kernel durations from the rocprofv3 kernel trace of a --staircase-only run")
+    ap.add_argument("--summarize-attention-trace", metavar="CSV", nargs="+",
+                    help="no GPU: per (context, M) kernel durations from the rocprofv3 kernel trace of an "
+                         "--attention-only run, then optional counter-collection CSVs of the same command")
     ap.add_argument("--summarize-counters", metavar="CSV", nargs="+",
                     help="no GPU: per-kernel counter means from rocprofv3 counter-collection CSVs")
     ap.add_argument("--gemm-only", action="store_true",
@@ -532,6 +593,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (sharding is "
               "described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_attention_trace:
+        paths = args.summarize_attention_trace
+        print(json.dumps(summarize_attention_trace(paths[0], paths[1:])), flush=True)
+        return
     if args.summarize_counters:
         print(json.dumps(summarize_counters(args.summarize_counters), indent=1), flush=True)
         return
