@@ -81,7 +81,37 @@ void k_gemm_lds(GemmArgs g) {
   gemm_unit_lds<MB, R>(g, blockIdx.x, blockIdx.y, lds);
 }
 
+// The wide-M variant: 1 wave per SIMD with 4 row tiles per wave, 2 with 2.
+template <int MB, int R>
+__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(R >= 4 ? 1 : 2)))
+void k_gemm_wide(GemmArgs g) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  if ((int)blockIdx.x >= g.nrb) return;  // grid padding
+  if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
+  gemm_unit_wide<MB, R>(g, blockIdx.x, blockIdx.y, lds);
+}
+
 typedef void (*GemmKernel)(GemmArgs);
+
+GemmKernel pick_wide_kernel(int mb, int r) {
+  switch (mb * 16 + r) {
+    case 3 * 16 + 2: return k_gemm_wide<3, 2>;
+    case 4 * 16 + 2: return k_gemm_wide<4, 2>;
+    case 5 * 16 + 2: return k_gemm_wide<5, 2>;
+    case 6 * 16 + 2: return k_gemm_wide<6, 2>;
+    case 7 * 16 + 2: return k_gemm_wide<7, 2>;
+    case 8 * 16 + 2: return k_gemm_wide<8, 2>;
+    case 4 * 16 + 4: return k_gemm_wide<4, 4>;
+    case 8 * 16 + 4: return k_gemm_wide<8, 4>;
+    default: return nullptr;
+  }
+}
+
+// LDS of the wide variant: one k-tile of activations, or the work-group's
+// tile sums (which reuse it) if larger, plus the ticket slot.
+size_t wide_variant_bytes(int mb, int r) {
+  return std::max((size_t)mb * 8 * ACT_FRAG_BYTES, (size_t)WG_WAVES * r * mb * 64 * sizeof(f32x4)) + 16;
+}
 
 GemmKernel pick_lds_kernel(int mb, int r) {
   switch (mb * 16 + r) {
@@ -189,7 +219,10 @@ static bool parse_bound(const char *tok, int open, int *out) {
 // Every M of the rule's range has a compiled kernel for its kernel and R.
 static bool rule_has_kernels(const TileRule &t) {
   for (int mb = (t.m_lo + 15) / 16; mb <= (t.m_hi + 15) / 16; ++mb) {
-    if (t.lds ? !pick_lds_kernel(mb, t.r) : !ring_depth(mb, t.r, 4)) return false;
+    const bool ok = t.lds == 2 ? pick_wide_kernel(mb, t.r) != nullptr
+                  : t.lds == 1 ? pick_lds_kernel(mb, t.r) != nullptr
+                               : ring_depth(mb, t.r, 4) != 0;
+    if (!ok) return false;
   }
   return true;
 }
@@ -224,14 +257,16 @@ int parse_tile_table(const char *text, TileRule *rules, int *n_rules) {
     TileRule t;
     if (!parse_bound(tok[1].c_str(), 1, &t.nrt_lo) || !parse_bound(tok[2].c_str(), 1 << 30, &t.nrt_hi) ||
         !parse_bound(tok[3].c_str(), 1, &t.nkt_lo) || !parse_bound(tok[4].c_str(), 1 << 30, &t.nkt_hi) ||
-        !parse_bound(tok[5].c_str(), 1, &t.m_lo) || !parse_bound(tok[6].c_str(), CHUNK_M, &t.m_hi))
+        !parse_bound(tok[5].c_str(), 1, &t.m_lo) || !parse_bound(tok[6].c_str(), NVFP4V_MAX_M, &t.m_hi))
       return NVFP4V_E_TABLE;
-    if (tok[7] == "lds") t.lds = 1;
+    if (tok[7] == "wide") t.lds = 2;
+    else if (tok[7] == "lds") t.lds = 1;
     else if (tok[7] == "reg") t.lds = 0;
     else return NVFP4V_E_TABLE;
     if (!parse_bound(tok[8].c_str(), 0, &t.r) || !parse_bound(tok[9].c_str(), 0, &t.ksplit)) return NVFP4V_E_TABLE;
     if (t.nrt_lo < 1 || t.nrt_lo > t.nrt_hi || t.nkt_lo < 1 || t.nkt_lo > t.nkt_hi || t.m_lo < 1 ||
-        t.m_lo > t.m_hi || t.m_hi > CHUNK_M || t.ksplit < 1 || t.ksplit > 64 || !rule_has_kernels(t))
+        t.m_lo > t.m_hi || t.m_hi > (t.lds == 2 ? NVFP4V_MAX_M : CHUNK_M) || t.ksplit < 1 || t.ksplit > 64 ||
+        !rule_has_kernels(t))
       return NVFP4V_E_TABLE;
     rules[n++] = t;
   }
@@ -290,7 +325,11 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
   }
   if (const char *ov = std::getenv("NVFP4V_PLAN")) {
     int r = 0, k2 = 0;
-    if (std::sscanf(ov, "n:r=%d,ks=%d", &r, &k2) == 2 && pick_lds_kernel(p->mblocks, r)) {
+    if (std::sscanf(ov, "w:r=%d,ks=%d", &r, &k2) == 2 && pick_wide_kernel(p->mblocks, r)) {
+      p->lds = 2;
+      p->rb = r;
+      want_ks = k2 > 0 ? k2 : 1;
+    } else if (std::sscanf(ov, "n:r=%d,ks=%d", &r, &k2) == 2 && pick_lds_kernel(p->mblocks, r)) {
       p->lds = 1;
       p->rb = r;
       want_ks = k2 > 0 ? k2 : 1;
@@ -302,7 +341,8 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
       if (std::sscanf(ov, "r=%*d,ks=%*d,d=%d", &d2) == 1 && d2 >= 1) want_d = d2;
     }
   }
-  if (p->lds && !pick_lds_kernel(p->mblocks, p->rb)) p->lds = 0, p->rb = 2;
+  if (p->lds == 2 && !pick_wide_kernel(p->mblocks, p->rb)) p->lds = 0, p->rb = 2;
+  if (p->lds == 1 && !pick_lds_kernel(p->mblocks, p->rb)) p->lds = 0, p->rb = 2;
   if (!p->lds && !ring_depth(p->mblocks, p->rb, 4)) p->rb = 4;
   p->depth = p->lds ? 0 : ring_depth(p->mblocks, p->rb, want_d);
   const int64_t rows_per_group = p->lds ? (int64_t)WG_WAVES * p->rb : p->rb;
@@ -313,8 +353,9 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p) {
     p->ktiles_per_split = per;
     p->ksplit = p->grid_y = (nkt + per - 1) / per;
   }
-  p->lds_bytes = p->lds ? lds_variant_bytes(p->mblocks, p->rb)
-                       : (size_t)WG_WAVES * p->rb * p->mblocks * 64 * sizeof(f32x4) + 16;
+  p->lds_bytes = p->lds == 2 ? wide_variant_bytes(p->mblocks, p->rb)
+                : p->lds    ? lds_variant_bytes(p->mblocks, p->rb)
+                            : (size_t)WG_WAVES * p->rb * p->mblocks * 64 * sizeof(f32x4) + 16;
   finish_grid(ctx, p);
   return NVFP4V_OK;
 }
@@ -380,13 +421,17 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
     const size_t need = (size_t)p.ksplit * (size_t)m * (size_t)(L.nrt * ROWS_PER_TILE);
     if (need > ctx->partial_floats || (size_t)p.nrb > ctx->n_counters) return NVFP4V_E_WORKSPACE;
   }
-  GemmKernel kern = p.lds ? pick_lds_kernel(p.mblocks, p.rb) : pick_kernel(p.mblocks, p.rb, p.depth);
+  GemmKernel kern = p.lds == 2 ? pick_wide_kernel(p.mblocks, p.rb)
+                  : p.lds      ? pick_lds_kernel(p.mblocks, p.rb)
+                               : pick_kernel(p.mblocks, p.rb, p.depth);
   if (!kern) return NVFP4V_E_INVALID_ARG;
+  if (m > CHUNK_M && p.lds != 2) return NVFP4V_E_INVALID_ARG;  // only the wide unit takes > 64 rows
   if (fault_injected()) return NVFP4V_E_FAULT;
   GemmArgs g;
   g.act = act;
   g.M = (int)m;
   g.act_bytes = (int)act_packed_bytes(m, k);
+  g.act_blk1 = m > CHUNK_M ? (int)act_block_bytes(CHUNK_M, k) : 0;
   g.W = (const uint8_t *)packed;
   g.N = (int)n;
   g.nrt = (int)L.nrt;
@@ -406,8 +451,18 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
   return hip_status(ctx, hipGetLastError());
 }
 
+// Whether the tile table gives an M-row call (M > 64) one launch of the wide
+// unit over both packed blocks of rows.
+static bool wide_rows(const nvfp4v_ctx *ctx, int64_t m, int64_t k, int64_t n) {
+  if (m <= CHUNK_M) return false;
+  Layout L;
+  Plan p;
+  return make_layout(n, k, &L) && make_plan(ctx, L, m, &p) == NVFP4V_OK && p.lds == 2;
+}
+
 int launch_gemm_rows(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
                      int64_t n, float ts, float *c, hipStream_t stream) {
+  if (wide_rows(ctx, m, k, n)) return launch_gemm(ctx, act, m, k, packed, n, ts, c, stream);
   int rc = NVFP4V_OK;
   for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
     const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
@@ -430,8 +485,10 @@ int launch_pack_rows(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, u
 
 // Workspace checks of the plan of every block of rows of an M-row call.
 static int check_rows_workspace(const nvfp4v_ctx *ctx, const Layout &L, int64_t m) {
+  const bool wide = wide_rows(ctx, m, L.k, L.n);
   for (int64_t r0 = 0; r0 < m; r0 += CHUNK_M) {
-    const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
+    const int64_t mc = wide ? m : std::min<int64_t>(CHUNK_M, m - r0);
+    if (wide && r0 > 0) break;
     Plan p;
     const int rc = make_plan(ctx, L, mc, &p);
     if (rc) return rc;
@@ -525,16 +582,19 @@ extern "C" int nvfp4v_describe_plan(nvfp4v_ctx *ctx, int64_t n, int64_t k, int64
   if (m < 1 || m > NVFP4V_MAX_M) return NVFP4V_E_M_RANGE;
   Layout L;
   if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
-  // M > 64 runs one launch per block of 64 rows: describe the first block's
-  // plan and the number of launches.
-  const int64_t blocks = (m + CHUNK_M - 1) / CHUNK_M;
+  // M > 64 runs one launch of the wide unit if the table says so, else one
+  // launch per block of 64 rows: then the first block's plan and the number
+  // of launches.
+  const bool wide = wide_rows(ctx, m, k, n);
+  const int64_t blocks = wide ? 1 : (m + CHUNK_M - 1) / CHUNK_M;
   Plan p;
-  int rc = make_plan(ctx, L, std::min<int64_t>(m, CHUNK_M), &p);
+  int rc = make_plan(ctx, L, wide ? m : std::min<int64_t>(m, CHUNK_M), &p);
   if (rc) return rc;
   char blk[48] = "";
   if (blocks > 1) snprintf(blk, sizeof(blk), " launches=%lld (64-row blocks)", (long long)blocks);
   snprintf(buf, len, "mfma16x16x32 %s mblocks=%d r=%d depth=%d waves=%d grid=%dx%d ksplit=%d kt/split=%d lds=%zu exchange=%s%s",
-           p.lds ? "act-in-lds/waves-split-n" : "waves-split-k", p.mblocks, p.rb, p.depth, p.waves,
+           p.lds == 2 ? "wide-m/waves-split-n" : p.lds ? "act-in-lds/waves-split-n" : "waves-split-k", p.mblocks,
+           p.rb, p.depth, p.waves,
            p.grid_x, p.grid_y, p.ksplit, p.ktiles_per_split, p.lds_bytes,
            p.ksplit == 1 ? "none" : p.xcd_local ? "xcd-l2" : "memory", blk);
   return NVFP4V_OK;

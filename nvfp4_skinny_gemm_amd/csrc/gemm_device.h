@@ -258,6 +258,10 @@ __device__ inline void epilogue(const f32x4 *red, int nw, int tid, int M, int N,
 struct GemmArgs {
   const uint8_t *act;  // packed activations
   int M, act_bytes;
+  // M > 64 (the wide unit only): the rows come as two packed blocks, rows
+  // 0..63 at `act` and rows 64.. at act + act_blk1 bytes (the layout
+  // pack_activations writes for more than 64 rows).
+  int act_blk1 = 0;
   const uint8_t *W;  // packed weights
   int N, nrt, nkt, kts_per_split, ksplit;
   float ts;
@@ -653,6 +657,146 @@ __device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
   // Each wave's tiles into slice 0 of the sums (tile wave * R + r), then the
   // shared tail (split-K exchange, epilogue).
   lds_barrier_wg();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
+  __syncthreads();
+  unit_tail<MB, RT, 1, true>(g, rb, ks, g.ksplit, red, tid);
+}
+
+// The wide-M unit (33..128 rows): like gemm_unit_lds, the 4 waves split N
+// (wave w owns R of the work-group's 4R row tiles) and walk the same k-tiles,
+// with each k-tile's packed activations (MB x 8 KiB) staged once per
+// work-group into LDS. The difference is the order of the products: per group
+// of 8 codes, a wave dequantises its R row tiles once and then runs them
+// against every 16-row block's fragment, read from LDS one at a time. A
+// fragment is reused across R row tiles and a dequantised weight across MB
+// blocks, so neither the fragments of all MB blocks (MB x 32 VGPRs) nor a
+// second dequant is needed. One LDS slot: the next k-tile's activations wait
+// in registers (MB / 2 16-byte chunks per thread) until every wave has
+// finished reading the slot; two work-group barriers per k-tile.
+template <int MB, int R>
+__device__ inline void gemm_unit_wide(const GemmArgs &g, int rb, int ks, uint8_t *lds) {
+  constexpr int RT = WG_WAVES * R;
+  constexpr int SLOT = MB * 8 * ACT_FRAG_BYTES;       // one k-tile of packed activations
+  constexpr int PER_THREAD = SLOT / WG_THREADS / 16;  // 16-byte chunks per thread
+  static_assert(SLOT % (WG_THREADS * 16) == 0, "staging split");
+  const int nrt = g.nrt, nkt = g.nkt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt0 = rb * RT + wave * R;
+  const int kA = ks * g.kts_per_split;
+  const int n = min(nkt, kA + g.kts_per_split) - kA;  // k-tiles of the unit (>= 1)
+  const int stripe_bytes = nkt * TILE_BYTES;
+  __amdgpu_buffer_rsrc_t rs[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rt = rt0 + r;
+    const uint8_t *base = g.W + (size_t)min(rt, nrt - 1) * (size_t)stripe_bytes;
+    rs[r] = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, rt < nrt ? stripe_bytes : 0,
+                                              RAW_BUFFER_FLAGS);
+  }
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.act, (short)0, g.act_bytes, RAW_BUFFER_FLAGS);
+
+  // The slot holds [row block][fragment q][lane]; thread t moves chunks
+  // c * 256 + t, i.e. row block c / 2, second half of its fragments if c is
+  // odd. Row blocks 0..3 come from the first packed block of 64 rows (B0 of
+  // them per k-tile), the rest from the second (MB - 4 per k-tile).
+  constexpr int B0 = MB < 4 ? MB : 4;
+  uint4 stage[PER_THREAD];
+  auto stage_load = [&](int j) {
+    const int kt = kA + j;
+#pragma unroll
+    for (int c = 0; c < PER_THREAD; ++c) {
+      const int mb = c / 2;
+      const int off = mb < B0 ? (kt * B0 + mb) * 8 * ACT_FRAG_BYTES
+                              : g.act_blk1 + (kt * (MB - B0) + (mb - B0)) * 8 * ACT_FRAG_BYTES;
+      const int base = j < n ? off + ((c & 1) * WG_THREADS + tid) * 16 : OOB;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(ra, base, 0, 0);
+      __builtin_memcpy(&stage[c], &x, 16);
+    }
+  };
+  auto stage_store = [&]() {
+    uint4 *dst = reinterpret_cast<uint4 *>(lds);
+#pragma unroll
+    for (int c = 0; c < PER_THREAD; ++c) dst[c * WG_THREADS + tid] = stage[c];
+  };
+  const uint4 *afr = reinterpret_cast<const uint4 *>(lds);
+
+  f32x4 acc[R][MB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[r][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Products of one k-tile: for each half C and group j of 8 codes, R
+  // dequantised weight fragments against MB activation fragments.
+  auto compute = [&](const WTile (&W)[R]) {
+    float sc[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) scales4(W[r].s, sc[r]);
+#pragma unroll
+    for (int C = 0; C < 2; ++C)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 wf[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t cw = j == 0 ? W[r].c[C].x : j == 1 ? W[r].c[C].y : j == 2 ? W[r].c[C].z : W[r].c[C].w;
+          wf[r] = dequant8(cw, sc[r][2 * C + (j >> 1)]);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const uint4 x = afr[(mb * 8 + 4 * C + j) * 64 + lane];
+          bf16x8 b;
+          __builtin_memcpy(&b, &x, 16);
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[r], b, acc[r][mb], 0, 0, 0);
+        }
+      }
+  };
+
+  WTile w0[R], w1[R];
+  stage_load(0);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_wtile(w0[r], rs[r], kA, true, lane);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_wtile(w1[r], rs[r], kA + 1, n > 1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Iteration i: every wave has finished reading k-tile i - 1 (barrier), the
+  // slot takes k-tile i from the staging registers, which then request
+  // k-tile i + 1; after a second barrier the slot is read; the weights of
+  // k-tile i + 2 go into the ring registers the products have just freed.
+#define NVFP4V_WIDE_STEP(W)                                                                         \
+  {                                                                                                 \
+    __syncthreads();                                                                                \
+    stage_store();                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                              \
+    stage_load(i + 1);                                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                              \
+    lds_barrier_wg();                                                                               \
+    compute(W);                                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                              \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) load_wtile(W[r], rs[r], kA + i + 2, i + 2 < n, lane); \
+    __builtin_amdgcn_sched_barrier(0);                                                              \
+  }
+  int i = 0;
+  for (; i + 1 < n; i += 2) {
+    NVFP4V_WIDE_STEP(w0)
+    ++i;
+    NVFP4V_WIDE_STEP(w1)
+    --i;
+  }
+  if (i < n) NVFP4V_WIDE_STEP(w0)
+#undef NVFP4V_WIDE_STEP
+
+  // The tiles' sums reuse the LDS (slice 0, tile wave * R + r), then the
+  // shared tail (split-K exchange, epilogue).
+  f32x4 *red = reinterpret_cast<f32x4 *>(lds);
+  __syncthreads();
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll

@@ -256,13 +256,16 @@ def test_checked_in_table_is_the_built_in_one(lib):
     "arch gfx950\nrule 1 * 1 * 1 64 wmma 2 1\n",      # unknown kernel
     "arch gfx950\nrule 1 * 1 * 1 64 reg 3 1\n",       # R with no kernel
     "arch gfx950\nrule 1 * 1 * 1 64 lds 2 1\n",       # lds R = 2 is built up to 32 rows only
-    "arch gfx950\nrule 1 * 1 * 1 65 reg 2 1\n",       # M beyond the API's range
+    "arch gfx950\nrule 1 * 1 * 1 65 reg 2 1\n",       # more than 64 rows in a register-variant launch
+    "arch gfx950\nrule 1 * 1 * 65 129 wide 2 1\n",    # M beyond the API's range
+    "arch gfx950\nrule 1 * 1 * 1 32 wide 2 1\n",      # the wide unit is built from 33 rows
     "arch gfx950\nrule 5 4 1 * 1 64 reg 2 1\n",       # empty range
     "arch gfx950\nrule 1 * 1 * 1 64 reg 2 0\n",       # no K split
     "arch gfx950\nrule 1 * 1 * 1 64 reg 2\n",         # missing field
     "arch gfx950\nrule 1 * 1 * x 64 reg 2 1\n",       # not a number
     "arch gfx950\n" + "rule 1 * 1 * 1 64 reg 2 1\n" * 65,  # too many rules
-], ids=["no-arch", "arch", "kernel", "r", "lds-r", "m", "range", "ks", "fields", "number", "count"])
+], ids=["no-arch", "arch", "kernel", "r", "lds-r", "m", "wide-m", "wide-lo", "range", "ks", "fields", "number",
+        "count"])
 def test_bad_tile_table_is_refused(lib, tmp_path, text):
     ctx = FakeCtx().ptr
     f = tmp_path / "bad.txt"
@@ -273,6 +276,25 @@ def test_bad_tile_table_is_refused(lib, tmp_path, text):
     out = ctypes.c_void_p()
     assert lib.nvfp4v_create(ctypes.byref(out), 0, str(f).encode()) == nv.E_TABLE
     assert not out.value
+
+
+def test_wide_rows_in_one_launch(lib, tmp_path):
+    """Above 64 rows the built-in table gives gate or up alone (1088 row tiles)
+    and gate|up fused (2176) one launch of the wide unit, and every other shape
+    one launch per block of 64 rows; a table file can move a shape to the wide
+    unit."""
+    ctx = FakeCtx().ptr
+    for m in (65, 100, 128):
+        assert "wide-m" in plan(lib, ctx, 17408, 5120, m) and "launches" not in plan(lib, ctx, 17408, 5120, m)
+        assert "wide-m" in plan(lib, ctx, 34816, 5120, m) and "ksplit=1" in plan(lib, ctx, 34816, 5120, m)
+        assert "launches=2 (64-row blocks)" in plan(lib, ctx, 5120, 17408, m)
+        assert "launches=2 (64-row blocks)" in plan(lib, ctx, 5120, 5120, m)
+    assert "wide-m" not in plan(lib, ctx, 17408, 5120, 64)
+    f = tmp_path / "down_wide.txt"
+    f.write_text("arch gfx950\nrule 300 330 60 70 65 128 wide 2 4\n")
+    assert lib.nvfp4v_load_tile_table(ctx, str(f).encode()) == nv.OK
+    got = plan(lib, ctx, 5120, 17408, 100)
+    assert "wide-m" in got and "mblocks=7" in got and "ksplit=4" in got and "launches" not in got
 
 
 def test_missing_tile_table_file(lib, tmp_path):

@@ -287,6 +287,30 @@ def test_plan_variants(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
         assert_parity(oracle_mod, c, c_ref[:m], s_ref[:m], "plan %s M=%d" % (plan, m))
 
 
+@pytest.mark.parametrize("plan", ["w:r=2,ks=1", "w:r=2,ks=3", "w:r=2,ks=18", "w:r=4,ks=1", "w:r=4,ks=2"])
+def test_wide_unit_plans(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
+    """The wide-M unit (one k-tile of activations in LDS, read one 16-row block
+    at a time; M up to 128 in one launch over both packed 64-row blocks) at
+    every row-block count it is built for, with split K (18 pieces: one k-tile
+    each) and ragged row tiles; R = 4 is built for 4 and 8 row blocks."""
+    torch = torch_cuda
+    n, k = 272, 4608   # 17 row tiles, 18 k-tiles
+    g = np.random.default_rng(37)
+    codes, scales = random_codes_scales(g, n, k)
+    a = synth.activations_bf16(128, k, seed=8, outliers=True)
+    c_ref, s_ref = oracle_mod.gemm(a, codes, scales, ts=0.5)
+    packed = pack_dev(torch, ctx, codes, scales, n, k)
+    a_dev = bf16_dev(torch, a)
+    monkeypatch.setenv("NVFP4V_PLAN", plan)
+    ms = (64, 128) if "r=4" in plan else (33, 48, 64, 65, 80, 96, 100, 112, 128)
+    for m in ms:
+        d = ctx.describe_plan(n, k, m)
+        log("plan %s M=%d: %s" % (plan, m, d))
+        assert "wide-m" in d and "launches" not in d
+        c = ctx.verify_gemm(a_dev[:m].contiguous(), packed, n, k, ts=0.5).cpu().numpy()
+        assert_parity(oracle_mod, c, c_ref[:m], s_ref[:m], "plan %s M=%d" % (plan, m))
+
+
 def test_dispatch_probe_enables_xcd_exchange(torch_cuda, ctx):
     """On MI355X (one partition, 8 XCDs dealt work-groups round-robin by id) the
     probe at create turns on the split-K exchange through one XCD's L2; the
