@@ -176,10 +176,12 @@ int nvfp4v_unpack(nvfp4v_ctx *ctx, const void *packed_dev, int64_t n, int64_t k,
  *              aligned, K % 8 == 0 for that alignment to hold per row
  *   packed_dev nvfp4v_pack output for the N x K weights, 16-byte aligned
  *   c_dev      fp32, row-major [M][N], 16-byte aligned; fully overwritten
- * M in 1..128. Does not allocate; safe to capture in a HIP graph. Two kernels
- * run per block of 64 rows: the block of A is packed into the context's
- * buffer (K up to 131072, else WORKSPACE), then the GEMM over it (rows are
- * independent, so M > 64 reads the weights once per block).
+ * M in 1..128. Does not allocate; safe to capture in a HIP graph. A is packed
+ * into the context's 16 MiB buffer (all M rows at once when they fit, else
+ * one block of 64 rows at a time; K up to 131072, else WORKSPACE), then the
+ * GEMM runs over it. For M > 64, where the tile table names the wide unit,
+ * one launch covers all rows; otherwise one launch per block of 64 rows, in
+ * turn.
  * Errors: INVALID_ARG, SHAPE, M_RANGE, ALIGN, WORKSPACE, HIP, FAULT. */
 int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_t k,
                        const void *packed_dev, int64_t n, float ts, float *c_dev,
@@ -271,7 +273,8 @@ int nvfp4v_tree_attention_plan(nvfp4v_ctx *ctx, int64_t ctx_len, int64_t m, int 
  *   nvfp4v_pack_activations: a_dev bf16 [M][K] row-major -> act_dev (16-byte
  *     aligned, nvfp4v_act_packed_bytes bytes). Errors: INVALID_ARG, M_RANGE,
  *     SHAPE, ALIGN, HIP, FAULT.
- *   nvfp4v_verify_gemm_pa: as nvfp4v_verify_gemm, with A given packed. */
+ *   nvfp4v_verify_gemm_pa: as nvfp4v_verify_gemm (the same launches for
+ *     M > 64), with A given packed. */
 size_t nvfp4v_act_packed_bytes(int64_t m, int64_t k);
 int nvfp4v_pack_activations(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_t k,
                             void *act_dev, hipStream_t stream);

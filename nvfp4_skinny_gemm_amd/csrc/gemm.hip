@@ -543,8 +543,14 @@ extern "C" int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m,
   int rc = check_rows_workspace(ctx, L, m);
   if (rc) return rc;
   if (fault_injected()) return NVFP4V_E_FAULT;
-  // One block of rows at a time through the context's buffer (stream order
-  // keeps a block's GEMM ahead of the next block's packing).
+  // All rows packed at once when they fit the context's buffer, so that more
+  // than 64 rows can take the wide unit's single launch; else one block of
+  // rows at a time (stream order keeps a block's GEMM ahead of the next
+  // block's packing).
+  if (act_packed_bytes(m, k) <= ctx->act_bytes) {
+    rc = launch_pack_rows(ctx, a, m, k, ctx->act, stream);
+    return rc ? rc : launch_gemm_rows(ctx, ctx->act, m, k, packed, n, ts, c, stream);
+  }
   for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
     const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
     rc = launch_pack_act(ctx, a + r0 * k, mc, k, ctx->act, stream);

@@ -311,6 +311,50 @@ def test_wide_unit_plans(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
         assert_parity(oracle_mod, c, c_ref[:m], s_ref[:m], "plan %s M=%d" % (plan, m))
 
 
+def test_row_blocks_equal_separate_calls(torch_cuda, ctx):
+    """Above 64 rows, shapes outside the wide unit run one launch per 64-row
+    block over activations packed all at once: bitwise equal to the two blocks
+    called one at a time, eagerly, pre-packed, and in graph replays with split
+    eager calls in between (the 5120 x 17408 down projection splits K in 3 at
+    both block sizes)."""
+    torch = torch_cuda
+    n, k, m = 5120, 17408, 100
+    g = np.random.default_rng(43)
+    codes, scales = random_codes_scales(g, n, k)
+    packed = pack_dev(torch, ctx, codes, scales, n, k)
+    a = bf16_dev(torch, synth.activations_bf16(m, k, seed=12, outliers=True))
+    d = ctx.describe_plan(n, k, m)
+    log("M=%d: %s | block 1: %s" % (m, d, ctx.describe_plan(n, k, m - 64)))
+    assert "launches=2" in d and "ksplit=3" in d and "ksplit=3" in ctx.describe_plan(n, k, m - 64)
+    ref = torch.cat([ctx.verify_gemm(a[:64], packed, n, k, ts=0.5),
+                     ctx.verify_gemm(a[64:].contiguous(), packed, n, k, ts=0.5)])
+    act = ctx.pack_activations(a)
+    for rep in range(2):
+        c = ctx.verify_gemm(a, packed, n, k, ts=0.5)
+        c_pa = ctx.verify_gemm_pa(act, m, k, packed, n, ts=0.5)
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int32), ref.view(torch.int32)), "eager %d" % rep
+        assert torch.equal(c_pa.view(torch.int32), ref.view(torch.int32)), "pre-packed %d" % rep
+    out = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ctx.verify_gemm_pa(act, m, k, packed, n, ts=0.5, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        ctx.verify_gemm_pa(act, m, k, packed, n, ts=0.5, out=out)
+    for rep in range(4):
+        out.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), "replay %d" % rep
+        c = ctx.verify_gemm(a[:64], packed, n, k, ts=0.5)
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int32), ref[:64].view(torch.int32)), "eager after replay %d" % rep
+    assert ctx.device_status() == 0
+
+
 def test_dispatch_probe_enables_xcd_exchange(torch_cuda, ctx):
     """On MI355X (one partition, 8 XCDs dealt work-groups round-robin by id) the
     probe at create turns on the split-K exchange through one XCD's L2; the

@@ -106,7 +106,7 @@ def mode_ctx(ctx, request):
 
 
 @pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
-@pytest.mark.parametrize("m", [1, 8, 16, 33, 64, 65, 128])
+@pytest.mark.parametrize("m", [1, 8, 16, 33, 64, 65, 120, 128])
 def test_pass_equals_composition(torch_cuda, mode_ctx, m):
     torch, ctx = torch_cuda, mode_ctx
     H, I, L = 256, 512, 3
@@ -206,19 +206,19 @@ def test_graph_replays_equal_eager(torch_cuda, mode_ctx):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("m", [8, 16, 24, 32])
+@pytest.mark.parametrize("m", [8, 16, 24, 32, 100, 120])
 def test_graph_replays_equal_eager_full_size(torch_cuda, ctx, m):
     """Full-size layers in the chained schedule, whose tile table splits K at
     these row counts (down at 8; gate|up and down at 16; down at 24 and 32) and
     exchanges the partial sums through one XCD's L2: graph replays equal the
     eager pass bitwise, with split eager GEMMs on the same context in between
     (they share the arrival counters), and no row block reports pieces on two
-    XCDs."""
+    XCDs. Above 64 rows the pass runs one 64-row block after the other."""
     torch = torch_cuda
     H, I, L = 5120, 17408, 2
     packed, arr = small_stack(torch, ctx, L, H, I, seed=3)
-    h0 = torch.from_numpy(synth.activations_bf16(64, H, seed=8).view(np.int16)).cuda().view(torch.bfloat16)
-    d_in = torch.from_numpy(synth.activations_bf16(64, I, seed=9).view(np.int16)).cuda().view(torch.bfloat16)
+    h0 = torch.from_numpy(synth.activations_bf16(128, H, seed=8).view(np.int16)).cuda().view(torch.bfloat16)
+    d_in = torch.from_numpy(synth.activations_bf16(128, I, seed=9).view(np.int16)).cuda().view(torch.bfloat16)
     ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
     eager = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
     ctx.verify_pass(arr, H, I, h0[:m], ws, eager)
