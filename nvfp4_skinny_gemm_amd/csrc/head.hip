@@ -20,10 +20,12 @@
 // bytes a lane feeds to MFMA i = 2 p + c are dwords 2c, 2c + 1 of load p: the
 // same k order (64 h + 8 i + e) as the packed activations' fragment i.
 //
-// Kernel (k_head): the 4 waves of a work-group split N. A wave owns R row
-// tiles over all of K and needs no cross-wave reduction; its weight tiles and
-// activation fragments stream through a two-deep register ring (loads past
-// the matrix return zeros). E4M3 -> bf16 is exact (4 significant bits, range
+// Kernels: the 4 waves of a work-group split N. A wave owns R row tiles over
+// all of K and needs no cross-wave reduction; its weight tiles stream through
+// a two-deep register ring (loads past the matrix return zeros). The
+// activations reach the waves either through one copy per work-group in LDS
+// (k_head_lds, the default) or through each wave's own two-deep ring of
+// fragment loads (k_head). E4M3 -> bf16 is exact (4 significant bits, range
 // 2^-9 .. 448): v_cvt_pk_f32_fp8 and the high halves packed with v_perm_b32.
 #include <algorithm>
 #include <cmath>
@@ -164,6 +166,128 @@ void k_head(HeadArgs g) {
   }
 }
 
+// The same head with the activations staged in LDS once per work-group
+// instead of once per wave: per k-tile every thread moves MB x 32 bytes of
+// the packed activations (read two k-tiles ahead into registers, written one
+// k-tile ahead into a two-slot LDS ring), and each wave reads its MFMA
+// fragments from LDS. One work-group barrier per k-tile, so every wave runs
+// the whole loop, also one whose row tiles lie past the matrix (its weight
+// loads return zeros and it writes nothing).
+template <int MB, int R>
+__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(1, head_waves_per_simd<MB>())))
+void k_head_lds(HeadArgs g) {
+  constexpr int SLOT = MB * 8 * ACT_FRAG_BYTES;       // one k-tile of packed activations
+  constexpr int PER_THREAD = SLOT / WG_THREADS / 16;  // 16-byte chunks per thread (2 MB)
+  __shared__ __align__(16) uint8_t lds[2 * SLOT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt0 = ((int)blockIdx.x * WG_WAVES + wave) * R;
+  const int n = g.nkt;
+  const int stripe = n * HEAD_TILE_BYTES;
+  __amdgpu_buffer_rsrc_t rs[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rt = rt0 + r;
+    const uint8_t *base = g.W + (size_t)min(rt, g.nrt - 1) * (size_t)stripe;
+    rs[r] = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, rt < g.nrt ? stripe : 0,
+                                              RAW_BUFFER_FLAGS);
+  }
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.act, (short)0, g.act_bytes, RAW_BUFFER_FLAGS);
+
+  // k-tile j's packed block is contiguous (SLOT bytes at j * SLOT); thread t
+  // moves chunks t, t + 256, ... of it. Rows >= M are zeros in the block.
+  auto stage_load = [&](uint4 (&v)[PER_THREAD], int j) {
+    const int base = j < n ? j * SLOT : OOB;
+#pragma unroll
+    for (int c = 0; c < PER_THREAD; ++c) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(ra, base + (c * WG_THREADS + tid) * 16, 0, 0);
+      __builtin_memcpy(&v[c], &x, 16);
+    }
+  };
+  auto stage_store = [&](const uint4 (&v)[PER_THREAD], int slot) {
+    uint4 *dst = reinterpret_cast<uint4 *>(lds + slot * SLOT);
+#pragma unroll
+    for (int c = 0; c < PER_THREAD; ++c) dst[c * WG_THREADS + tid] = v[c];
+  };
+  auto frags = [&](bf16x8 (&b)[MB][8], int slot) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(lds + slot * SLOT);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 x = src[(mb * 8 + q) * 64 + lane];
+        __builtin_memcpy(&b[mb][q], &x, 16);
+      }
+  };
+
+  f32x4 acc[R][MB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[r][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  HTile w0[R], w1[R];
+  uint4 s0[PER_THREAD], s1[PER_THREAD];
+  stage_load(s0, 0);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_htile(w0[r], rs[r], 0, true, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_load(s1, 1);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_htile(w1[r], rs[r], 1, n > 1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store(s0, 0);
+  stage_load(s0, 2);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Iteration i: barrier (slot i % 2 holds k-tile i, the other slot is free),
+  // fragments of k-tile i, k-tile i + 1 into the free slot, k-tile i + 3's
+  // activations requested, compute, then k-tile i + 2's weights requested
+  // into the registers the compute has just freed.
+#define NVFP4V_HEAD_STEP(W, S_NEXT, SLOT_I)                                                 \
+  {                                                                                           \
+    lds_barrier_wg();                                                                         \
+    bf16x8 b[MB][8];                                                                          \
+    frags(b, SLOT_I);                                                                         \
+    stage_store(S_NEXT, 1 - SLOT_I);                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    stage_load(S_NEXT, i + 3);                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) compute_htile<MB>(W[r], b, acc[r]);        \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) load_htile(W[r], rs[r], i + 2, i + 2 < n, lane); \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+  }
+  int i = 0;
+  for (; i + 1 < n; i += 2) {
+    NVFP4V_HEAD_STEP(w0, s1, 0)
+    ++i;
+    NVFP4V_HEAD_STEP(w1, s0, 1)
+    --i;
+  }
+  if (i < n) NVFP4V_HEAD_STEP(w0, s1, 0)
+#undef NVFP4V_HEAD_STEP
+
+  // Lane L holds rows 16 rt + 4 (L >> 4) + e (e = 0..3) of column 16 mb + (L & 15).
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rt = rt0 + r;
+    if (rt >= g.nrt) break;
+    const int n0 = rt * 16 + 4 * (lane >> 4);
+    const f32x4 sc = *reinterpret_cast<const f32x4 *>(g.scales + n0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = mb * 16 + (lane & 15);
+      if (m >= g.M) continue;
+      float *crow = g.C + (size_t)m * (size_t)g.N;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n0 + e < g.N) crow[n0 + e] = sc[e] * acc[r][mb][e];
+    }
+  }
+}
+
 bool head_shape_ok(int64_t n, int64_t k) {
   // k <= 2^22 keeps a stripe (nkt * 4096 bytes) below 64 MiB, well inside a
   // buffer resource's 32-bit range; n <= 2^28 keeps row indices in int.
@@ -177,9 +301,10 @@ size_t head_bytes(int64_t n, int64_t k) {
 
 typedef void (*HeadKernel)(HeadArgs);
 
-// R row tiles per wave: 2 (measured on MI355X for 151936 x 5120: 124 / 142 /
-// 188 us at M = 1 / 16 / 32, against 135 / 146 / 187 with R = 4 and 139 / 169
-// / 242 with R = 1). NVFP4V_HEAD_R=1|2|4 overrides (4 only at M <= 16).
+// R row tiles per wave: 2 (measured on MI355X for 151936 x 5120 with the LDS
+// stage: 121 / 134 / 154 us at M = 1 / 16 / 32, against 120 / 134 / 168 with
+// R = 1 and 137 / 145 / 154 with R = 4). NVFP4V_HEAD_R=1|2|4 overrides (4 only
+// at M <= 16).
 int head_r(int mblocks) {
   if (const char *ov = std::getenv("NVFP4V_HEAD_R")) {
     const int r = std::atoi(ov);
@@ -195,6 +320,25 @@ HeadKernel pick_head(int mblocks, int r) {
     case 3: return r == 1 ? k_head<3, 1> : k_head<3, 2>;
     default: return r == 1 ? k_head<4, 1> : k_head<4, 2>;
   }
+}
+
+HeadKernel pick_head_lds(int mblocks, int r) {
+  switch (mblocks) {
+    case 1: return r == 1 ? k_head_lds<1, 1> : r == 2 ? k_head_lds<1, 2> : k_head_lds<1, 4>;
+    case 2: return r == 1 ? k_head_lds<2, 1> : k_head_lds<2, 2>;
+    case 3: return r == 1 ? k_head_lds<3, 1> : k_head_lds<3, 2>;
+    default: return r == 1 ? k_head_lds<4, 1> : k_head_lds<4, 2>;
+  }
+}
+
+// Activations staged in LDS per work-group (k_head_lds) or loaded per wave
+// (k_head): LDS at every M, measured on MI355X for 151936 x 5120 at R = 2
+// (121 / 134 / 142 / 154 / 198 / 239 us at M = 1 / 16 / 17 / 32 / 48 / 64,
+// against 122 / 144 / 165 / 191 / 243 / 279 with per-wave loads).
+// NVFP4V_HEAD_LDS=0|1 overrides.
+bool head_lds() {
+  if (const char *ov = std::getenv("NVFP4V_HEAD_LDS")) return std::atoi(ov) != 0;
+  return true;
 }
 
 // One launch over a block of at most 64 rows (m <= CHUNK_M).
@@ -214,7 +358,8 @@ int launch_head_block(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k,
   const int r = head_r(mblocks);
   const int rows_per_wg = WG_WAVES * r;
   const int grid = (g.nrt + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL(pick_head(mblocks, r), dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, g);
+  const HeadKernel kern = head_lds() ? pick_head_lds(mblocks, r) : pick_head(mblocks, r);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, g);
   return hip_status(ctx, hipGetLastError());
 }
 

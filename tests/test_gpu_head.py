@@ -74,23 +74,28 @@ def test_head_parity_quantised(torch_cuda, ctx, oracle_mod, n, k, m):
     assert torch.equal(c, c2)
 
 
+@pytest.mark.parametrize("lds", ["0", "1"])
 @pytest.mark.parametrize("r", ["1", "2", "4"])
-def test_head_tilings_bitwise_equal(torch_cuda, ctx, monkeypatch, r):
-    """Every wave sums its rows over all of K in the same order, so the row
-    tiles per wave change nothing in C."""
+def test_head_tilings_bitwise_equal(torch_cuda, ctx, monkeypatch, r, lds):
+    """Every wave sums its rows over all of K in the same order, so neither the
+    row tiles per wave nor where the activations are staged (each wave's own
+    loads, or one copy per work-group in LDS) change anything in C; one to
+    four row blocks of M, ragged N and K."""
     torch = torch_cuda
     n, k = 301, 1296
     codes = synth.fp8_codes(n, k, seed=9)
     scales = synth.fp8_row_scales(n, seed=9)
     packed = torch.from_numpy(nv.fp8_pack_host(codes, scales)).cuda()
-    for m in (3, 16, 30):
+    for m in (3, 16, 30, 40, 64):
         ad = bf16_dev(torch, synth.activations_bf16(m, k, seed=m, stream="headr"))
+        monkeypatch.setenv("NVFP4V_HEAD_LDS", "0")
         monkeypatch.delenv("NVFP4V_HEAD_R", raising=False)
         base = ctx.fp8_head_gemm(ad, packed, n, k)
         monkeypatch.setenv("NVFP4V_HEAD_R", r)
+        monkeypatch.setenv("NVFP4V_HEAD_LDS", lds)
         other = ctx.fp8_head_gemm(ad, packed, n, k)
         torch.cuda.synchronize()
-        assert torch.equal(base, other), "m=%d r=%s" % (m, r)
+        assert torch.equal(base, other), "m=%d r=%s lds=%s" % (m, r, lds)
 
 
 @pytest.fixture(scope="module")

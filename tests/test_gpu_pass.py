@@ -284,9 +284,10 @@ def workspace_views(ws, m, H, I, L):
 
 
 @pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
-@pytest.mark.parametrize("m", [16, 24, 32])
+@pytest.mark.parametrize("m", [1, 8, 9, 16, 24, 32])
 def test_full_size_phases_against_oracle(torch_cuda, mode_ctx, oracle_mod, m):
-    """Two full-size layers (H = 5120, I = 17408). For the last layer, every
+    """Two full-size layers (H = 5120, I = 17408), at M in every regime of the
+    tile table up to two row blocks (1..8, 9..16, 17..32). For the last layer, every
     GEMM's fp32 output is checked against the oracle on 384 sampled weight
     rows, fed with the packed activations the kernels read, taken back from
     the workspace; every glue step (and the hand-over between layers) is
