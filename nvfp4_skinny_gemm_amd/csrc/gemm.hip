@@ -57,14 +57,14 @@ namespace {
 
 using namespace nvfp4v::dev;
 
-template <int MB, int R, int D>
-__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MB, R, D>())))
+template <int MB, int R, int D, bool A2 = false>
+__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd<MB, R, D, A2>())))
 void k_gemm(GemmArgs g) {
   extern __shared__ __align__(16) f32x4 red[];
   if ((int)blockIdx.x >= g.nrb) return;  // grid padding
   if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
   const int ks = blockIdx.y, kA = ks * g.kts_per_split;
-  gemm_unit<MB, R, D>(g, blockIdx.x, kA, min(g.nkt, kA + g.kts_per_split), ks, g.ksplit, red);
+  gemm_unit<MB, R, D, A2>(g, blockIdx.x, kA, min(g.nkt, kA + g.kts_per_split), ks, g.ksplit, red);
 }
 
 template <int MB, int R>
@@ -132,7 +132,15 @@ size_t lds_variant_bytes(int mb, int r) {
 // Ring depth per (row blocks, R): 2 by default, 1 where two copies of the
 // fragments do not fit. Depths 3-4 are reachable only through NVFP4V_PLAN
 // (measured slower in the pass at 1-16 rows, kept for the override's tests).
+// The one-deep ring with two-deep activation fragments (gemm_unit's A2) for
+// two row blocks of four row tiles; NVFP4V_A2=0 keeps the plain one-deep ring.
+static bool use_a2() {
+  const char *ov = std::getenv("NVFP4V_A2");
+  return !ov || std::atoi(ov) != 0;
+}
+
 GemmKernel pick_kernel(int mb, int r, int d) {
+  if (mb == 2 && r == 4 && d == 1 && use_a2()) return k_gemm<2, 4, 1, true>;
   switch ((mb * 16 + r) * 8 + d) {
     case (1 * 16 + 1) * 8 + 2: return k_gemm<1, 1, 2>;
     case (1 * 16 + 2) * 8 + 2: return k_gemm<1, 2, 2>;

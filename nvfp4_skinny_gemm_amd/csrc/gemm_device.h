@@ -147,9 +147,9 @@ __device__ inline void compute_reload_wtile(WTile &t, const bf16x8 (&b)[MB][8], 
 // Occupancy target (waves per SIMD) for the register allocator: three when
 // the ring (D k-tiles of R weight tiles and MB fragment blocks), the
 // accumulators and ~40 working registers fit in 168 VGPRs, else two.
-template <int MB, int R, int D>
+template <int MB, int R, int D, bool A2 = false>
 constexpr int waves_per_simd() {
-  return (D * (R * 9 + MB * 32) + R * MB * 4 + 40) <= 168 ? 3 : 2;
+  return ((A2 ? R * 9 + 2 * MB * 32 : D * (R * 9 + MB * 32)) + R * MB * 4 + 40) <= 168 ? 3 : 2;
 }
 
 __device__ inline uint16_t bf16_bits(float x) {
@@ -466,7 +466,7 @@ __device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, int ksplit, 
 // buffer of WG_WAVES * R * MB * 64 f32x4. Every thread of the work-group calls
 // this with the same arguments; it returns with the LDS buffer free for the
 // next unit.
-template <int MB, int R, int D>
+template <int MB, int R, int D, bool A2 = false>
 __device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int ks, int ksplit, f32x4 *red) {
   const uint8_t *__restrict__ act = g.act;
   const int M = g.M, act_bytes = g.act_bytes, nrt = g.nrt, nkt = g.nkt;
@@ -497,6 +497,48 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[r][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (A2) {
+    // One-deep weight ring (each tile reloaded in halves while it is
+    // consumed) with the activation fragments two deep: k-tile i + 1's
+    // fragments are requested before k-tile i is computed, so their L2
+    // latency hides behind a whole k-tile of work instead of stalling the
+    // next one. For MB x R where two full rings do not fit in registers.
+    static_assert(D == 1, "the two-deep activation ring goes with a one-deep weight ring");
+    WTile w[R];
+    bf16x8 a[2][MB][8];
+    load_afrag<MB>(a[0], ra, kbeg, 0 < n, M, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_wtile(w[r], rs[r], kbeg, 0 < n, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    load_afrag<MB>(a[1], ra, kbeg + 1, 1 < n, M, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    // Step d of iteration i computes k-tile i + d from (w, a[d]), reloading w
+    // with k-tile i + d + 1 and then a[d] with k-tile i + d + 2; every step
+    // issues the same loads in the same order (zeros past the range).
+    int i = 0;
+    for (; i + 2 <= n; i += 2) {
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          compute_reload_wtile<MB>(w[r], a[d], acc[r], rs[r], kbeg + i + d + 1, i + d + 1 < n, lane);
+        load_afrag<MB>(a[d], ra, kbeg + i + d + 2, i + d + 2 < n, M, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (i < n) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) compute_wtile<MB>(w[r], a[0], acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
+    __syncthreads();
+    unit_tail<MB, R, WG_WAVES>(g, rb, ks, ksplit, red, tid);
+    return;
+  }
 
   // A ring of D k-tiles (weights and activation fragments) per wave: slot d
   // holds k-tiles kbeg + d, kbeg + d + D, ...; each slot is refilled D

@@ -287,6 +287,33 @@ def test_plan_variants(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
         assert_parity(oracle_mod, c, c_ref[:m], s_ref[:m], "plan %s M=%d" % (plan, m))
 
 
+@pytest.mark.parametrize("plan", ["r=4,ks=1", "r=4,ks=3", "r=4,ks=18"])
+def test_two_deep_activation_ring(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
+    """Two row blocks at R = 4 take the one-deep weight ring with two-deep
+    activation fragments: each wave sums its k-tiles in the same order as the
+    plain one-deep ring (NVFP4V_A2=0), so C is bitwise the same, and it agrees
+    with the oracle (odd and even k-tile counts per wave, one k-tile per
+    work-group at 18 pieces, ragged row tiles)."""
+    torch = torch_cuda
+    n, k = 272, 4608
+    g = np.random.default_rng(47)
+    codes, scales = random_codes_scales(g, n, k)
+    a = synth.activations_bf16(32, k, seed=11, outliers=True)
+    c_ref, s_ref = oracle_mod.gemm(a, codes, scales, ts=0.75)
+    packed = pack_dev(torch, ctx, codes, scales, n, k)
+    a_dev = bf16_dev(torch, a)
+    monkeypatch.setenv("NVFP4V_PLAN", plan)
+    for m in (17, 24, 32):
+        monkeypatch.setenv("NVFP4V_A2", "1")
+        c2 = ctx.verify_gemm(a_dev[:m], packed, n, k, ts=0.75)
+        monkeypatch.setenv("NVFP4V_A2", "0")
+        c1 = ctx.verify_gemm(a_dev[:m], packed, n, k, ts=0.75)
+        torch.cuda.synchronize()
+        log("plan %s M=%d: %s" % (plan, m, ctx.describe_plan(n, k, m)))
+        assert torch.equal(c1.view(torch.int32), c2.view(torch.int32)), "plan %s M=%d" % (plan, m)
+        assert_parity(oracle_mod, c2.cpu().numpy(), c_ref[:m], s_ref[:m], "A2 plan %s M=%d" % (plan, m))
+
+
 @pytest.mark.parametrize("plan", ["w:r=2,ks=1", "w:r=2,ks=3", "w:r=2,ks=18", "w:r=4,ks=1", "w:r=4,ks=2"])
 def test_wide_unit_plans(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
     """The wide-M unit (one k-tile of activations in LDS, read one 16-row block
