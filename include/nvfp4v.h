@@ -257,9 +257,10 @@ int nvfp4v_tree_attention(nvfp4v_ctx *ctx, const uint16_t *q_dev, const uint16_t
                           void *ws_dev, size_t ws_bytes, hipStream_t stream);
 
 /* The chunking nvfp4v_tree_attention uses for a shape on the context's GPU
- * (chunks per key/value head: one resident wave of work-groups over the CUs,
- * at least 352 positions and at most 64 chunks; positions per chunk), for
- * reports. Errors: INVALID_ARG, SHAPE, M_RANGE, HIP. */
+ * (chunks per key/value head: one work-group per CU, or every work-group slot
+ * for two column blocks over chunks longer than 2048 positions; at least 352
+ * positions and at most 64 chunks; positions per chunk), for reports.
+ * Errors: INVALID_ARG, SHAPE, M_RANGE, HIP. */
 int nvfp4v_tree_attention_plan(nvfp4v_ctx *ctx, int64_t ctx_len, int64_t m, int hq, int hkv, int d,
                                int *nchunks, int *chunk);
 

@@ -434,17 +434,28 @@ constexpr int MIN_CHUNK_POS = 352;
 
 int attn_nb(int64_t m, int hq, int hkv) { return (int64_t)(hq / hkv) * m <= 16 ? 1 : 2; }
 
-// Chunks per key/value head: one resident wave of work-groups over the GPU
-// (slots = work-groups per CU the kernel fits x CUs), at least 352 positions a
-// chunk, at most 64 chunks.
-void attn_plan(int64_t ctx_len, int64_t m, int hq, int hkv, int slots, AttnPlan *p) {
+// Chunks per key/value head: one work-group per CU (chunks = CUs / Hkv), or,
+// with two column blocks and chunks longer than 2048 positions, every
+// work-group slot the kernel has (its work-groups per CU x CUs); at least 352
+// positions a chunk, at most 64 chunks. Measured at 40 heads (µs, M = 16 / 32):
+// one work-group per CU (6 chunks) against two (12 chunks) 25.5 / 35.2 vs
+// 28.9 / 37.6 at 4k, 38.8 / 50.6 vs 43.6 / 53.3 at 8k, 68.7 / 83.8 vs
+// 74.5 / 81.4 at 16k and 122.3 / 146.4 vs 131.7 / 137.8 at 32k. A wave of the
+// one-block kernel keeps two groups of keys and values in flight, so one wave
+// per SIMD streams at the full rate, and a head's last work-group then merges
+// half as many records; the two-block kernel keeps one group in flight and
+// needs the second work-group per CU once chunks are long.
+void attn_plan(int64_t ctx_len, int64_t m, int hq, int hkv, int per_cu, int cus, AttnPlan *p) {
   p->nb = attn_nb(m, hq, hkv);
   const int64_t P = ctx_len + m;
-  int64_t nch = std::max<int64_t>(1, slots / hkv);
+  int64_t nch = std::max<int64_t>(1, cus / hkv);
+  if (p->nb == 2 && P > 2048 * nch) nch = std::max<int64_t>(1, (int64_t)per_cu * cus / hkv);
   nch = std::min<int64_t>({nch, (P + MIN_CHUNK_POS - 1) / MIN_CHUNK_POS, (int64_t)MAX_CHUNKS});
-  // NVFP4V_ATTN_CHUNKS=<n> overrides the chunk count (for measurements).
+  // NVFP4V_ATTN_CHUNKS=<n> overrides the chunk count (for measurements; at
+  // least one 32-position group per chunk, at most 64 chunks).
   if (const char *env = std::getenv("NVFP4V_ATTN_CHUNKS"))
-    if (std::atoi(env) > 0) nch = std::min<int64_t>(std::atoi(env), (P + MIN_CHUNK_POS - 1) / MIN_CHUNK_POS);
+    if (std::atoi(env) > 0)
+      nch = std::min<int64_t>({(int64_t)std::atoi(env), (P + GROUP_POS - 1) / GROUP_POS, (int64_t)MAX_CHUNKS});
   nch = std::max<int64_t>(nch, 1);
   int64_t chunk = (P + nch - 1) / nch;
   chunk = (chunk + GROUP_POS - 1) / GROUP_POS * GROUP_POS;
@@ -465,13 +476,14 @@ size_t attn_ws_bytes(const AttnPlan &p, int hkv) {
   return 256 + (size_t)hkv * p.nchunks * p.rec_floats * sizeof(float);
 }
 
-// Work-group slots on the GPU for the kernel of `nb` column blocks.
-int attn_slots(nvfp4v_ctx *ctx, int nb, int *slots) {
-  int per_cu = 0;
+// Work-groups per CU the kernel of `nb` column blocks fits, and the CUs.
+int attn_slots(nvfp4v_ctx *ctx, int nb, int *per_cu, int *cus) {
+  int n = 0;
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, nb == 1 ? (const void *)k_tree_attn<1> : (const void *)k_tree_attn<2>, ATTN_THREADS, 0);
+      &n, nb == 1 ? (const void *)k_tree_attn<1> : (const void *)k_tree_attn<2>, ATTN_THREADS, 0);
   if (e != hipSuccess) return hip_status(ctx, e);
-  *slots = std::max(1, per_cu) * std::max(1, ctx->num_cus);
+  *per_cu = std::max(1, n);
+  *cus = std::max(1, ctx->num_cus);
   return NVFP4V_OK;
 }
 
@@ -533,11 +545,11 @@ extern "C" int nvfp4v_tree_attention(nvfp4v_ctx *ctx, const uint16_t *q, const u
     if (pr < 0 || pr >= i) return NVFP4V_E_INVALID_ARG;
     a.vis[i] = a.vis[pr] | (1u << i);
   }
-  int slots = 0;
-  rc = attn_slots(ctx, attn_nb(m, hq, hkv), &slots);
+  int per_cu = 0, cus = 0;
+  rc = attn_slots(ctx, attn_nb(m, hq, hkv), &per_cu, &cus);
   if (rc) return rc;
   AttnPlan p;
-  attn_plan(ctx_len, m, hq, hkv, slots, &p);
+  attn_plan(ctx_len, m, hq, hkv, per_cu, cus, &p);
   if (ws_bytes < attn_ws_bytes(p, hkv)) return NVFP4V_E_WORKSPACE;
   if (fault_injected()) return NVFP4V_E_FAULT;
   a.q = q;
@@ -569,11 +581,11 @@ extern "C" int nvfp4v_tree_attention_plan(nvfp4v_ctx *ctx, int64_t ctx_len, int6
   if (!ctx || !nchunks || !chunk) return NVFP4V_E_INVALID_ARG;
   int rc = check_attn_shape(std::max<int64_t>(32, (ctx_len + m + 31) / 32 * 32), ctx_len, m, hq, hkv, d);
   if (rc) return rc;
-  int slots = 0;
-  rc = attn_slots(ctx, attn_nb(m, hq, hkv), &slots);
+  int per_cu = 0, cus = 0;
+  rc = attn_slots(ctx, attn_nb(m, hq, hkv), &per_cu, &cus);
   if (rc) return rc;
   AttnPlan p;
-  attn_plan(ctx_len, m, hq, hkv, slots, &p);
+  attn_plan(ctx_len, m, hq, hkv, per_cu, cus, &p);
   *nchunks = p.nchunks;
   *chunk = p.chunk;
   return NVFP4V_OK;
