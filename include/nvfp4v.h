@@ -235,7 +235,7 @@ int nvfp4v_kv_write(nvfp4v_ctx *ctx, const uint16_t *k_rows_dev, const uint16_t 
                     int64_t pos0, int hkv, int d, int64_t cap, uint16_t *k_cache_dev,
                     uint16_t *v_cache_dev, hipStream_t stream);
 
-/* Workspace of nvfp4v_tree_attention (0 for a bad shape). Its first 256 bytes
+/* Workspace of nvfp4v_tree_attention (0 for a bad shape). Its first 1024 bytes
  * are arrival tickets that must be zero before the first call (hipMemset once);
  * every call leaves them zero. */
 size_t nvfp4v_tree_attention_workspace_bytes(int64_t ctx_len, int64_t m, int hq, int hkv, int d);
@@ -257,9 +257,11 @@ int nvfp4v_tree_attention(nvfp4v_ctx *ctx, const uint16_t *q_dev, const uint16_t
                           void *ws_dev, size_t ws_bytes, hipStream_t stream);
 
 /* The chunking nvfp4v_tree_attention uses for a shape on the context's GPU
- * (chunks per key/value head: one work-group per CU, or every work-group slot
- * for two column blocks over chunks longer than 2048 positions; at least 352
- * positions and at most 64 chunks; positions per chunk), for reports.
+ * (chunks per key/value head: one work-group per CU, where more than 16 query
+ * columns over a context of up to 8192 positions take one work-group per
+ * 16-column block, and longer contexts with more than 16 columns every
+ * work-group slot once chunks exceed 2048 positions; at least 352 positions
+ * and at most 64 chunks; positions per chunk), for reports.
  * Errors: INVALID_ARG, SHAPE, M_RANGE, HIP. */
 int nvfp4v_tree_attention_plan(nvfp4v_ctx *ctx, int64_t ctx_len, int64_t m, int hq, int hkv, int d,
                                int *nchunks, int *chunk);

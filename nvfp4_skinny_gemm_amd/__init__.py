@@ -479,7 +479,7 @@ class Context:
                        scale: float = None, out=None, ws=None, stream=None):
         """O fp32 [M, Hq, 128] of the tree rows q (bf16 [M, Hq, 128]) against the cached
         context (positions 0..ctx_len-1) and their own root paths (parent_rows: M ints,
-        -1 for row 0). `ws` (uint8, tree_attention_workspace_bytes, its first 256 bytes
+        -1 for row 0). `ws` (uint8, tree_attention_workspace_bytes, its first 1024 bytes
         zero before the first use) is allocated zeroed when not given."""
         import numpy as np
         import torch

@@ -74,6 +74,7 @@ struct AttnArgs {
   unsigned *cnt;       // [Hkv] arrival tickets (zero between calls)
   int64_t cap;         // cache capacity in positions (multiple of 32)
   int T, M, hq, hkv, group, P, chunk, nchunks;
+  int ncb;             // work-groups per (head, chunk), each NB column blocks of its own
   float scale;
   uint32_t vis[NVFP4V_ATTN_MAX_ROWS];  // bit j of vis[i]: row i sees tree row j
 };
@@ -102,7 +103,9 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.y, ci = blockIdx.x;
+  const int h = blockIdx.y, ci = blockIdx.x, z = blockIdx.z;
+  const int col0 = z * NB * 16;  // this work-group's first query column
+  const int hz = h * a.ncb + z;  // its record set and ticket
   const int g = lane >> 4, c16 = lane & 15;
   const int p0 = ci * a.chunk, p1 = min(a.P, p0 + a.chunk);
   const int ngroups = (p1 - p0 + GROUP_POS - 1) / GROUP_POS;
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
   int rowc[NB];  // query row of this lane's column, or -1 for a padding column
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
-    const int c = cb * 16 + c16;
+    const int c = col0 + cb * 16 + c16;
     rowc[cb] = c < ncols ? c % a.M : -1;
     const int qh = h * a.group + (c < ncols ? c / a.M : 0);
 #pragma unroll
@@ -264,16 +267,16 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
   if (a.nchunks == 1) {
     for (int it = tid; it < NB * DBLK * 64; it += ATTN_THREADS) {
       const int cb = it / (DBLK * 64), d = (it / 64) % DBLK, ln = it & 63;
-      const int c = cb * 16 + (ln & 15);
+      const int cl = cb * 16 + (ln & 15), c = col0 + cl;
       if (c >= ncols) continue;
       float mx = -INFINITY;
-      for (int w = 0; w < ATTN_WAVES; ++w) mx = fmaxf(mx, s_m[w][c]);
+      for (int w = 0; w < ATTN_WAVES; ++w) mx = fmaxf(mx, s_m[w][cl]);
       float l = 0.f;
       f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int w = 0; w < ATTN_WAVES; ++w) {
-        if (s_m[w][c] == -INFINITY) continue;
-        const float f = expf(s_m[w][c] - mx);
-        l += s_l[w][c] * f;
+        if (s_m[w][cl] == -INFINITY) continue;
+        const float f = expf(s_m[w][cl] - mx);
+        l += s_l[w][cl] * f;
         v += s_o[w][cb][d][ln] * f;
       }
       const float inv = 1.f / l;
@@ -286,9 +289,9 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
   }
 
   // The chunk's record, through memory (system scope: sc0 sc1 stores).
-  float *rec = a.rec + ((size_t)h * a.nchunks + ci) * record_floats<NB>();
+  float *rec = a.rec + ((size_t)hz * a.nchunks + ci) * record_floats<NB>();
   const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.rec + (size_t)h * a.nchunks * record_floats<NB>()), (short)0,
+      (void *)(a.rec + (size_t)hz * a.nchunks * record_floats<NB>()), (short)0,
       (int)((size_t)a.nchunks * record_floats<NB>() * sizeof(float)), RAW_BUFFER_FLAGS);
   const int rbase = ci * record_floats<NB>() * (int)sizeof(float);  // this record, bytes
   if (tid < NB * 16) {
@@ -302,12 +305,12 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
   }
   for (int it = tid; it < NB * DBLK * 64; it += ATTN_THREADS) {
     const int cb = it / (DBLK * 64), d = (it / 64) % DBLK, ln = it & 63;
-    const int c = cb * 16 + (ln & 15);
+    const int cl = cb * 16 + (ln & 15);
     float mx = -INFINITY;
-    for (int w = 0; w < ATTN_WAVES; ++w) mx = fmaxf(mx, s_m[w][c]);
+    for (int w = 0; w < ATTN_WAVES; ++w) mx = fmaxf(mx, s_m[w][cl]);
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int w = 0; w < ATTN_WAVES; ++w)
-      if (s_m[w][c] != -INFINITY) v += s_o[w][cb][d][ln] * expf(s_m[w][c] - mx);
+      if (s_m[w][cl] != -INFINITY) v += s_o[w][cb][d][ln] * expf(s_m[w][cl] - mx);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rr,
                                            rbase + (NB * 32 + it * 4) * (int)sizeof(float), 0, SYSTEM_AUX);
   }
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
-    const unsigned old = __hip_atomic_fetch_add(&a.cnt[h], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const unsigned old = __hip_atomic_fetch_add(&a.cnt[hz], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     s_last = old == (unsigned)(a.nchunks - 1) ? 1u : 0u;
   }
   __syncthreads();
@@ -345,10 +348,10 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
   __syncthreads();
   for (int it = tid; it < NB * DBLK * 64; it += ATTN_THREADS) {
     const int cb = it / (DBLK * 64), d = (it / 64) % DBLK, ln = it & 63;
-    const int c = cb * 16 + (ln & 15);
+    const int cl = cb * 16 + (ln & 15), c = col0 + cl;
     if (c >= ncols) continue;
     float mx = -INFINITY;
-    for (int k = 0; k < a.nchunks; ++k) mx = fmaxf(mx, s_ml[k * NB * 32 + c]);
+    for (int k = 0; k < a.nchunks; ++k) mx = fmaxf(mx, s_ml[k * NB * 32 + cl]);
     float l = 0.f;
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < a.nchunks; k0 += 8) {
@@ -366,10 +369,10 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
       for (int u = 0; u < 8; ++u) {
         const int k = k0 + u;
         if (k >= a.nchunks) break;
-        const float mk = s_ml[k * NB * 32 + c];
+        const float mk = s_ml[k * NB * 32 + cl];
         if (mk == -INFINITY) continue;
         const float f = expf(mk - mx);
-        l += s_ml[k * NB * 32 + NB * 16 + c] * f;
+        l += s_ml[k * NB * 32 + NB * 16 + cl] * f;
         v += part[u] * f;
       }
     }
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(ATTN_THREADS, 2) void k_tree_attn(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[r] = v[r] * inv;
   }
-  if (tid == 0) __hip_atomic_store(&a.cnt[h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (tid == 0) __hip_atomic_store(&a.cnt[hz], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // Rows [n][Hkv][D] (bf16) -> cache positions pos0 .. pos0 + n - 1, fragment
@@ -422,15 +425,23 @@ __global__ void k_kv_write(const uint16_t *__restrict__ krows, const uint16_t *_
 }
 
 struct AttnPlan {
-  int nb, nchunks, chunk;
+  int nb, ncb, nchunks, chunk;  // column blocks per work-group, work-groups per (head, chunk)
   size_t rec_floats;
 };
+// Arrival tickets at the start of the workspace: one per (head, work-group
+// of column blocks).
+constexpr size_t TICKET_BYTES = 1024;
 
 constexpr int MAX_CHUNKS = 64;
 // At least 352 positions a chunk (11 groups of 32, about three per wave):
 // measured at 40 heads, 1k context, M = 16 / 32: 14.9 / 21.3 us with 3 chunks
 // against 16.2 / 24.1 with 9 chunks of 128 and 20.4 / 31.2 with one.
 constexpr int MIN_CHUNK_POS = 352;
+// Contexts up to this many positions split two column blocks over two
+// work-groups, one per CU (3 chunks a head at 40 heads): measured at 40 heads
+// and M = 32, 21.2 / 26.2 / 36.3 / 52.7 us at 1k / 2k / 4k / 8k in one
+// work-group, 14.8 / 20.5 / 31.1 / 50.7 split.
+constexpr int64_t SPLIT_MAX_POS = 8192 + NVFP4V_ATTN_MAX_ROWS;
 
 int attn_nb(int64_t m, int hq, int hkv) { return (int64_t)(hq / hkv) * m <= 16 ? 1 : 2; }
 
@@ -447,9 +458,21 @@ int attn_nb(int64_t m, int hq, int hkv) { return (int64_t)(hq / hkv) * m <= 16 ?
 // needs the second work-group per CU once chunks are long.
 void attn_plan(int64_t ctx_len, int64_t m, int hq, int hkv, int per_cu, int cus, AttnPlan *p) {
   p->nb = attn_nb(m, hq, hkv);
+  p->ncb = 1;
   const int64_t P = ctx_len + m;
   int64_t nch = std::max<int64_t>(1, cus / hkv);
-  if (p->nb == 2 && P > 2048 * nch) nch = std::max<int64_t>(1, (int64_t)per_cu * cus / hkv);
+  // Two column blocks over a short context: one work-group per column block
+  // (each reads the chunk's keys and values; the twin, 8-congruent in id, on
+  // the same XCD), so that a wave keeps two groups in flight.
+  const char *split_env = std::getenv("NVFP4V_ATTN_SPLIT");
+  const bool split = p->nb == 2 && (split_env ? std::atoi(split_env) != 0 : P <= SPLIT_MAX_POS);
+  if (split) {
+    p->nb = 1;
+    p->ncb = 2;
+    nch = std::max<int64_t>(1, cus / (2 * hkv));
+  } else if (p->nb == 2 && P > 2048 * nch) {
+    nch = std::max<int64_t>(1, (int64_t)per_cu * cus / hkv);
+  }
   nch = std::min<int64_t>({nch, (P + MIN_CHUNK_POS - 1) / MIN_CHUNK_POS, (int64_t)MAX_CHUNKS});
   // NVFP4V_ATTN_CHUNKS=<n> overrides the chunk count (for measurements; at
   // least one 32-position group per chunk, at most 64 chunks).
@@ -469,11 +492,11 @@ size_t attn_ws_bound(int64_t ctx_len, int64_t m, int hq, int hkv) {
   const int64_t P = ctx_len + m;
   const int64_t nch = std::min<int64_t>((P + MIN_CHUNK_POS - 1) / MIN_CHUNK_POS, MAX_CHUNKS);
   const size_t rec = attn_nb(m, hq, hkv) == 1 ? record_floats<1>() : record_floats<2>();
-  return 256 + (size_t)hkv * (size_t)nch * rec * sizeof(float);
+  return TICKET_BYTES + (size_t)hkv * (size_t)nch * rec * sizeof(float);
 }
 
 size_t attn_ws_bytes(const AttnPlan &p, int hkv) {
-  return 256 + (size_t)hkv * p.nchunks * p.rec_floats * sizeof(float);
+  return TICKET_BYTES + (size_t)hkv * p.ncb * p.nchunks * p.rec_floats * sizeof(float);
 }
 
 // Work-groups per CU the kernel of `nb` column blocks fits, and the CUs.
@@ -557,7 +580,7 @@ extern "C" int nvfp4v_tree_attention(nvfp4v_ctx *ctx, const uint16_t *q, const u
   a.vc = v_cache;
   a.o = o;
   a.cnt = reinterpret_cast<unsigned *>(ws);
-  a.rec = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + 256);
+  a.rec = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + TICKET_BYTES);
   a.cap = cap;
   a.T = (int)ctx_len;
   a.M = (int)m;
@@ -567,8 +590,9 @@ extern "C" int nvfp4v_tree_attention(nvfp4v_ctx *ctx, const uint16_t *q, const u
   a.P = (int)(ctx_len + m);
   a.chunk = p.chunk;
   a.nchunks = p.nchunks;
+  a.ncb = p.ncb;
   a.scale = scale;
-  const dim3 grid((unsigned)p.nchunks, (unsigned)hkv);
+  const dim3 grid((unsigned)p.nchunks, (unsigned)hkv, (unsigned)p.ncb);
   if (p.nb == 1)
     hipLaunchKernelGGL(k_tree_attn<1>, grid, dim3(ATTN_THREADS), 0, stream, a);
   else

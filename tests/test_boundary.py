@@ -355,14 +355,15 @@ def test_attention_sizes():
     # caches: cap * Hkv * 128 bf16 each
     assert nv.kv_cache_bytes(64, 40) == 64 * 40 * 128 * 2
     assert nv.kv_cache_bytes(48, 40) == 0 and nv.kv_cache_bytes(64, 40, 64) == 0 and nv.kv_cache_bytes(0, 1) == 0
-    # workspace: 256 bytes of tickets + one record per (head, chunk), at most
-    # one chunk per 352 positions and 64 chunks per head
+    # workspace: 1024 bytes of tickets + one record per (head, chunk) and 16
+    # query columns, at most one chunk per 352 positions and 64 chunks per head
     one = nv.tree_attention_workspace_bytes(100, 16, 40, 40)
     rec1 = (16 * 2 + 8 * 64 * 4) * 4  # one 16-column block
-    assert one == 256 + 40 * 1 * rec1
-    assert nv.tree_attention_workspace_bytes(32768, 16, 40, 40) == 256 + 40 * 64 * rec1
+    assert one == 1024 + 40 * 1 * rec1
+    assert nv.tree_attention_workspace_bytes(32768, 16, 40, 40) == 1024 + 40 * 64 * rec1
     rec2 = (32 * 2 + 2 * 8 * 64 * 4) * 4
-    assert nv.tree_attention_workspace_bytes(1000, 17, 40, 40) == 256 + 40 * 3 * rec2  # 1017 positions
+    assert rec2 == 2 * rec1  # two blocks in one record, or two work-groups' records
+    assert nv.tree_attention_workspace_bytes(1000, 17, 40, 40) == 1024 + 40 * 3 * rec2  # 1017 positions
     assert nv.tree_attention_workspace_bytes(10, 33, 40, 40) == 0
     assert nv.tree_attention_workspace_bytes(10, 4, 40, 40, 64) == 0
 

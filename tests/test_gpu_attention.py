@@ -154,6 +154,46 @@ def test_graph_replay_equals_eager(torch_cuda, ctx):
         assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), "replay %d" % rep
 
 
+@pytest.mark.parametrize("case", [(1000, 32, 4, 4), (3000, 17, 40, 40), (5000, 24, 8, 8), (600, 8, 4, 1)],
+                         ids=["T1000-M32", "T3000-M17-40h", "T5000-M24", "T600-grouped"])
+def test_column_split_is_bitwise_neutral(torch_cuda, ctx, monkeypatch, case):
+    """Two column blocks in one work-group, or one work-group per block (each
+    then streams the chunk's keys and values itself, two groups in flight per
+    wave): every column's scores, softmax and sums are computed in the same
+    order, so at equal chunking O is bitwise the same; and it agrees with the
+    oracle either way (the split also graph-replays)."""
+    torch = torch_cuda
+    ctx_len, m, hq, hkv = case
+    q, k, v = synth.attention_inputs(m, hq, hkv, ctx_len, seed=11)
+    parent = synth.tree_parent_rows(m, seed=11)
+    cap = (ctx_len + m + 31) // 32 * 32
+    kc, vc = build_cache(torch, ctx, k, v, ctx_len, m, cap)
+    qd = dev_bf16(torch, q)
+    # equal chunking both ways (within the workspace's bound of one chunk per 352 positions)
+    monkeypatch.setenv("NVFP4V_ATTN_CHUNKS", str(min(3, -(-(ctx_len + m) // 352))))
+    outs = []
+    for split in ("0", "1"):
+        monkeypatch.setenv("NVFP4V_ATTN_SPLIT", split)
+        ws = torch.zeros(nv.tree_attention_workspace_bytes(ctx_len, m, hq, hkv), dtype=torch.uint8, device="cuda")
+        outs.append(ctx.tree_attention(qd, kc, vc, cap, ctx_len, hkv, parent, scale=1.0 / math.sqrt(128), ws=ws))
+        torch.cuda.synchronize()
+        if split == "1":
+            out = torch.empty_like(outs[-1])
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                ctx.tree_attention(qd, kc, vc, cap, ctx_len, hkv, parent, scale=1.0 / math.sqrt(128), ws=ws,
+                                   out=out)
+            for rep in range(2):
+                out.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(out.view(torch.int32), outs[-1].view(torch.int32)), "replay %d" % rep
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    o_ref, o_abs, o_e = att.tree_attention(q, k, v, parent, ctx_len, 1.0 / math.sqrt(128))
+    ok = att.within_tolerance(outs[1].cpu().numpy(), o_ref, o_abs, o_e)
+    assert ok.all(), "%d of %d outside the tolerance" % ((~ok).sum(), ok.size)
+
+
 def test_argument_errors(torch_cuda, ctx):
     import ctypes
 
