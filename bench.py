@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 H, I, LAYERS = 5120, 17408, 64
 BYTES_PER_WEIGHT = 0.5625  # 4-bit code + one E4M3 byte per 16 weights
 PEAK_HBM_GBS = 8000.0
-PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0  # dense fp16 and bf16 MFMA (the same peak)
 CLOCK_GHZ, SIMDS = 2.4, 1024  # 256 CUs x 4 SIMDs
 VALU_CYCLES = 4  # a wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles
 METRIC = "verify-pass µs and achieved HBM GB/s vs M (1..32), full 27B layer stack"

@@ -178,7 +178,7 @@ int nvfp4v_unpack(nvfp4v_ctx *ctx, const void *packed_dev, int64_t n, int64_t k,
  *   c_dev      fp32, row-major [M][N], 16-byte aligned; fully overwritten
  * M in 1..128. Does not allocate; safe to capture in a HIP graph. A is packed
  * into the context's 16 MiB buffer (all M rows at once when they fit, else
- * one block of 64 rows at a time; K up to 131072, else WORKSPACE), then the
+ * one block of 64 rows at a time; K up to 65536, else WORKSPACE), then the
  * GEMM runs over it. For M > 64, where the tile table names the wide unit,
  * one launch covers all rows; otherwise one launch per block of 64 rows, in
  * turn.
@@ -191,12 +191,15 @@ int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a_dev, int64_t m, int64_
  * serving loops, harnesses that forbid hipMalloc): nvfp4v_verify_gemm without a
  * context, on the current HIP device. It allocates nothing: its scratch (the
  * packed activations of one block of 64 rows, split-K partial sums and arrival
- * counters) is one file-scope device array of 16 MiB + 64 KiB that every GPU
+ * counters) is one file-scope device array of 24 MiB + 64 KiB that every GPU
  * the library runs on holds until the process ends. Limits: K such that a
- * block of 64 rows of packed activations fits 8 MiB (K <= 65536), and plans
- * whose split-K partials fit 8 MiB and use at most 4096 row blocks, else
- * WORKSPACE. It uses the built-in tile table and exchanges split-K partials
- * through memory; C equals nvfp4v_verify_gemm's bitwise. Every call on a GPU
+ * block of 64 rows of packed activations (both copies) fits 16 MiB
+ * (K <= 65536), and plans whose split-K partials fit 8 MiB and use at most
+ * 4096 row blocks, else WORKSPACE. It uses the built-in tile table and
+ * exchanges split-K partials through memory, one launch per block of 64 rows;
+ * C equals nvfp4v_verify_gemm's bitwise wherever that also runs one launch per
+ * block (always up to 64 rows; above, shapes the tile table gives the wide
+ * unit sum in another order and agree to the same tolerance). Every call on a GPU
  * shares that GPU's array (a small kernel clears its counters at the start of
  * each call): calls that overlap on one GPU (other streams, other threads)
  * race and must not be made. Errors: INVALID_ARG, SHAPE, M_RANGE, ALIGN,
@@ -271,8 +274,17 @@ int nvfp4v_tree_attention_plan(nvfp4v_ctx *ctx, int64_t ctx_len, int64_t m, int 
  * its glue kernels). nvfp4v_verify_gemm does this packing internally, into the
  * context's buffer, before each call. More than 64 rows are packed as
  * consecutive blocks of 64 rows (the last one shorter), each in the layout of
- * its own row count.
- *   nvfp4v_act_packed_bytes: bytes of the packed form of A[M][K] (0 if bad).
+ * its own row count. The packed form holds A twice in that order: the bf16
+ * values, then (half the packed size further on) each value times 2^8 as fp16
+ * where that conversion is exact (0, or magnitudes in [2^-25, 2^8)) and a NaN
+ * marker elsewhere. The GEMM computes from the fp16 copy, whose products with
+ * the dequantised weights are exact (an fp16 dequantisation costs one VALU
+ * operation per weight, the bf16 one two), and computes any work unit whose
+ * sums meet a marker again from the bf16 copy: C is the same, bitwise, as
+ * computed from the bf16 values alone (NVFP4V_F16=0 in the environment does
+ * that for every unit).
+ *   nvfp4v_act_packed_bytes: bytes of the packed form of A[M][K], both
+ *     copies (0 if bad).
  *   nvfp4v_pack_activations: a_dev bf16 [M][K] row-major -> act_dev (16-byte
  *     aligned, nvfp4v_act_packed_bytes bytes). Errors: INVALID_ARG, M_RANGE,
  *     SHAPE, ALIGN, HIP, FAULT.
@@ -414,8 +426,8 @@ int nvfp4v_glue_sum(nvfp4v_ctx *ctx, const float *x_dev, int64_t ldx, const floa
 
 /* Bytes of caller-owned device workspace nvfp4v_verify_pass needs for
  * n_layers layers (0 for bad arguments): the fp32 outputs of one layer plus
- * one block of packed bf16 activations per layer and GEMM (about 1 MiB per
- * layer at M = 16, H = 5120, I = 17408). */
+ * one block of packed activations (both copies) per layer and GEMM (about
+ * 2 MiB per layer at M = 16, H = 5120, I = 17408). */
 size_t nvfp4v_pass_workspace_bytes(int64_t m, int64_t hidden, int64_t inter, int n_layers);
 
 /* How nvfp4v_verify_pass schedules its GEMMs (per context; default CHAIN):

@@ -19,14 +19,23 @@
 //    range, a row tile past N or an activation row >= M gets an offset past the
 //    buffer's size, which returns zeros without a memory access. Straight-line
 //    loads keep the compiler's wait counts exact.
-//  * Dequantisation is exact: v_cvt_scalef32_pk_f32_fp4 turns two E2M1 codes
-//    into fp32 (with a unit scale; on gfx950 the instruction applies only the
-//    exponent of its scale operand), a fp32 multiply applies the E4M3 block
-//    scale (v_cvt_f32_fp8 decodes it), and the high halves are packed as bf16
-//    (an E2M1 value times an E4M3 scale has at most 6 significant bits and lies
-//    in [2^-10, 2688]).
-//  * v_mfma_f32_16x16x32_bf16 with the weights as the 16-row A operand and a
-//    16-row block of activations as the B operand, fp32 accumulation.
+//  * Dequantisation is exact, in fp16: v_cvt_scalef32_pk_f16_fp4 turns two
+//    E2M1 codes into fp16 (with a unit scale; on gfx950 the instruction applies
+//    only the exponent of its scale operand) and one v_pk_mul_f16 applies the
+//    E4M3 block scale, decoded to fp16 (an E2M1 value times an E4M3 scale has
+//    at most 6 significant bits and lies in [2^-10, 2688]): one VALU operation
+//    per weight.
+//  * v_mfma_f32_16x16x32_f16 with the weights as the 16-row A operand and a
+//    16-row block of activations as the B operand, fp32 accumulation. The
+//    activations come from the fp16 copy of the packed activations (internal.h:
+//    the bf16 values times 2^8, exact, or a NaN marker where fp16 cannot hold
+//    the value), so every product is exact and the sums are the bf16 products'
+//    sums times 2^8, scaled back at the end of the unit. A unit whose sums hold
+//    a NaN is computed again from the bf16 copy with the bf16 form of the
+//    dequantisation (v_cvt_scalef32_pk_f32_fp4, two fp32 multiplies, the high
+//    halves packed as bf16) and v_mfma_f32_16x16x32_bf16: C is bitwise what the
+//    bf16 path alone gives (on gfx950 the two MFMAs sum the same exact
+//    products identically).
 //  * The 4 waves' tiles are summed through LDS in wave order. With ksplit > 1
 //    the K pieces of a row block exchange partial tiles. By default (the
 //    create-time dispatch probe found that work-groups with linear ids
@@ -63,8 +72,10 @@ void k_gemm(GemmArgs g) {
   extern __shared__ __align__(16) f32x4 red[];
   if ((int)blockIdx.x >= g.nrb) return;  // grid padding
   if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
-  const int ks = blockIdx.y, kA = ks * g.kts_per_split;
-  gemm_unit<MB, R, D, A2>(g, blockIdx.x, kA, min(g.nkt, kA + g.kts_per_split), ks, g.ksplit, red);
+  const int ks = blockIdx.y, kA = ks * g.kts_per_split, kB = min(g.nkt, kA + g.kts_per_split);
+  if constexpr (MB <= F16_MAX_MB)
+    if (g.act16 && gemm_unit<MB, R, D, A2, true>(g, blockIdx.x, kA, kB, ks, g.ksplit, red)) return;
+  gemm_unit<MB, R, D, A2, false>(g, blockIdx.x, kA, kB, ks, g.ksplit, red);
 }
 
 template <int MB, int R>
@@ -78,7 +89,9 @@ void k_gemm_lds(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
   if ((int)blockIdx.x >= g.nrb) return;  // grid padding
   if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
-  gemm_unit_lds<MB, R>(g, blockIdx.x, blockIdx.y, lds);
+  if constexpr (MB <= F16_MAX_MB)
+    if (g.act16 && gemm_unit_lds<MB, R, true>(g, blockIdx.x, blockIdx.y, lds)) return;
+  gemm_unit_lds<MB, R, false>(g, blockIdx.x, blockIdx.y, lds);
 }
 
 // The wide-M variant: 1 wave per SIMD with 4 row tiles per wave, 2 with 2.
@@ -88,7 +101,9 @@ void k_gemm_wide(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
   if ((int)blockIdx.x >= g.nrb) return;  // grid padding
   if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
-  gemm_unit_wide<MB, R>(g, blockIdx.x, blockIdx.y, lds);
+  if constexpr (F16_WIDE)
+    if (g.act16 && gemm_unit_wide<MB, R, true>(g, blockIdx.x, blockIdx.y, lds)) return;
+  gemm_unit_wide<MB, R, false>(g, blockIdx.x, blockIdx.y, lds);
 }
 
 typedef void (*GemmKernel)(GemmArgs);
@@ -176,11 +191,12 @@ __global__ void k_xcd_probe(unsigned *out) {
     out[blockIdx.x + blockIdx.y * gridDim.x] = (unsigned)__builtin_amdgcn_s_getreg(XCC_ID_HWREG) & 0xFu;
 }
 
-// Row-major A -> packed activations: one thread per 16-byte chunk.
+// Row-major A -> packed activations: one thread per 16-byte chunk, into the
+// bf16 copy and, when act16 > 0, the fp16 copy act16 / 16 chunks further on.
 // `sync` (optional): the persistent pass's barrier words, zeroed here because
 // this kernel starts every pass (its grid always has more threads than words).
 __global__ void k_pack_act(const uint16_t *__restrict__ A, int M, int K, int mblocks, int nkt,
-                           uint4 *__restrict__ out, unsigned *sync) {
+                           uint4 *__restrict__ out, int64_t act16, unsigned *sync) {
   const int64_t total = (int64_t)nkt * mblocks * 8 * 64;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (sync && idx < PASS_SYNC_WORDS) sync[idx] = 0u;
@@ -196,6 +212,15 @@ __global__ void k_pack_act(const uint16_t *__restrict__ A, int M, int K, int mbl
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (row < M && k0 < K) v = *reinterpret_cast<const uint4 *>(A + (size_t)row * K + k0);
   out[idx] = v;
+  if (act16) {
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      h[i] = (uint32_t)f16_act_bits((uint16_t)(in[i] & 0xFFFFu)) |
+             ((uint32_t)f16_act_bits((uint16_t)(in[i] >> 16)) << 16);
+    out[idx + act16 / 16] = make_uint4(h[0], h[1], h[2], h[3]);
+  }
 }
 
 }  // namespace
@@ -400,19 +425,25 @@ int probe_dispatch(nvfp4v_ctx *ctx) {
   return NVFP4V_OK;
 }
 
+bool use_f16() {
+  const char *ov = std::getenv("NVFP4V_F16");
+  return !ov || std::atoi(ov) != 0;
+}
+
 int launch_pack_act(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
-                    hipStream_t stream, unsigned *sync) {
+                    size_t act16, hipStream_t stream, unsigned *sync) {
   const int mb = (int)((m + 15) / 16), nkt = (int)((k + 255) / 256);
   const int64_t total = (int64_t)nkt * mb * 8 * 64;
   int64_t blocks = (total + 255) / 256;
   if (sync) blocks = std::max<int64_t>(blocks, (PASS_SYNC_WORDS + 255) / 256);
   hipLaunchKernelGGL(k_pack_act, dim3((unsigned)blocks), dim3(256), 0, stream, a, (int)m, (int)k,
-                     mb, nkt, (uint4 *)act, sync);
+                     mb, nkt, (uint4 *)act, (int64_t)act16, sync);
   return hip_status(ctx, hipGetLastError());
 }
 
-int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
-                int64_t n, float ts, float *c, hipStream_t stream, const Epilogue &epi) {
+int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, size_t act16, int64_t m, int64_t k,
+                const void *packed, int64_t n, float ts, float *c, hipStream_t stream,
+                const Epilogue &epi) {
   Layout L;
   if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
   Plan p;
@@ -438,7 +469,8 @@ int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const
   GemmArgs g;
   g.act = act;
   g.M = (int)m;
-  g.act_bytes = (int)act_packed_bytes(m, k);
+  g.act_bytes = (int)act_copy_bytes(m, k);
+  g.act16 = (int)act16;
   g.act_blk1 = m > CHUNK_M ? (int)act_block_bytes(CHUNK_M, k) : 0;
   g.W = (const uint8_t *)packed;
   g.N = (int)n;
@@ -470,11 +502,12 @@ static bool wide_rows(const nvfp4v_ctx *ctx, int64_t m, int64_t k, int64_t n) {
 
 int launch_gemm_rows(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
                      int64_t n, float ts, float *c, hipStream_t stream) {
-  if (wide_rows(ctx, m, k, n)) return launch_gemm(ctx, act, m, k, packed, n, ts, c, stream);
+  const size_t act16 = use_f16() ? act_copy_bytes(m, k) : 0;
+  if (wide_rows(ctx, m, k, n)) return launch_gemm(ctx, act, act16, m, k, packed, n, ts, c, stream);
   int rc = NVFP4V_OK;
   for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
     const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
-    rc = launch_gemm(ctx, act, mc, k, packed, n, ts, c + r0 * n, stream);
+    rc = launch_gemm(ctx, act, act16, mc, k, packed, n, ts, c + r0 * n, stream);
     act += act_block_bytes(mc, k);
   }
   return rc;
@@ -482,10 +515,11 @@ int launch_gemm_rows(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, 
 
 int launch_pack_rows(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
                      hipStream_t stream) {
+  const size_t act16 = act_copy_bytes(m, k);
   int rc = NVFP4V_OK;
   for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
     const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
-    rc = launch_pack_act(ctx, a + r0 * k, mc, k, act, stream);
+    rc = launch_pack_act(ctx, a + r0 * k, mc, k, act, act16, stream);
     act += act_block_bytes(mc, k);
   }
   return rc;
@@ -547,7 +581,7 @@ extern "C" int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m,
   Layout L;
   if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
   if (!aligned16(a) || !aligned16(packed) || !aligned16(c)) return NVFP4V_E_ALIGN;
-  if (act_block_bytes(std::min<int64_t>(m, CHUNK_M), k) > ctx->act_bytes) return NVFP4V_E_WORKSPACE;
+  if (2 * act_block_bytes(std::min<int64_t>(m, CHUNK_M), k) > ctx->act_bytes) return NVFP4V_E_WORKSPACE;
   int rc = check_rows_workspace(ctx, L, m);
   if (rc) return rc;
   if (fault_injected()) return NVFP4V_E_FAULT;
@@ -559,10 +593,12 @@ extern "C" int nvfp4v_verify_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m,
     rc = launch_pack_rows(ctx, a, m, k, ctx->act, stream);
     return rc ? rc : launch_gemm_rows(ctx, ctx->act, m, k, packed, n, ts, c, stream);
   }
+  const bool f16 = use_f16();
   for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
     const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
-    rc = launch_pack_act(ctx, a + r0 * k, mc, k, ctx->act, stream);
-    if (!rc) rc = launch_gemm(ctx, ctx->act, mc, k, packed, n, ts, c + r0 * n, stream);
+    const size_t act16 = act_block_bytes(mc, k);
+    rc = launch_pack_act(ctx, a + r0 * k, mc, k, ctx->act, act16, stream);
+    if (!rc) rc = launch_gemm(ctx, ctx->act, f16 ? act16 : 0, mc, k, packed, n, ts, c + r0 * n, stream);
   }
   return rc;
 }

@@ -10,6 +10,8 @@ namespace nvfp4v {
 namespace dev {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -66,6 +68,108 @@ __device__ inline void scales4(uint32_t sw, float s[4]) {
   s[3] = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
 }
 
+// The fp16 dequantisation: two E2M1 codes -> fp16 (unit scale), times the
+// block scale as fp16 (ss: the scale in both halves) in one packed multiply. E4M3 scales are exact in fp16
+// (2^-9 is an fp16 normal), and so are their products with E2M1 values (at
+// most 6 significant bits in [2^-10, 2688]): one VALU operation per weight
+// against two for the bf16 form.
+__device__ inline f16x8 dequant8h(uint32_t codes, f16x2 ss) {
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss;
+  const f16x8 r = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  return r;
+}
+
+// A lane's dequantiser for one weight tile: its four block scales decoded
+// once, then dequant(codes, i) for the 8 codes under scale i. F16 selects the
+// fp16 form (fragments f16x8, v_mfma_f32_16x16x32_f16) over the bf16 form.
+template <bool F16> struct Dq;
+template <> struct Dq<false> {
+  typedef bf16x8 frag;
+  float s[4];
+  Dq() = default;
+  __device__ explicit Dq(uint32_t sw) { scales4(sw, s); }
+  __device__ frag operator()(uint32_t codes, int i) const { return dequant8(codes, s[i]); }
+};
+template <> struct Dq<true> {
+  typedef f16x8 frag;
+  f16x2 s01, s23;
+  Dq() = default;
+  __device__ explicit Dq(uint32_t sw) {
+    s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+    s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
+  }
+  __device__ frag operator()(uint32_t codes, int i) const {
+    // Whole-register selects and a broadcast shuffle (folded into the packed
+    // multiply's operand selection) keep the scales in registers.
+    const f16x2 p = (i >> 1) ? s23 : s01;
+    return dequant8h(codes, (i & 1) ? __builtin_shufflevector(p, p, 1, 1) : __builtin_shufflevector(p, p, 0, 0));
+  }
+};
+
+__device__ inline f32x4 mfma(const bf16x8 &w, const bf16x8 &a, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, a, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma(const f16x8 &w, const f16x8 &a, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(w, a, c, 0, 0, 0);
+}
+
+// The fp16 copy's value of a bf16 value: v * 2^ACT_F16_SHIFT as fp16 when
+// exact, else the marker (internal.h).
+__device__ inline uint16_t f16_act_bits(uint16_t bf) {
+  // ldexp, not a multiply: the compiler fuses a multiply with the conversion
+  // into v_fma_mix with a +0 addend, which turns -0 into +0.
+  const float a = __uint_as_float((uint32_t)bf << 16);
+  const _Float16 h = (_Float16)__builtin_ldexpf(a, ACT_F16_SHIFT);
+  const bool exact = __builtin_ldexpf((float)h, -ACT_F16_SHIFT) == a;  // false for NaN
+  uint16_t u;
+  __builtin_memcpy(&u, &h, 2);
+  return exact ? u : ACT_F16_MARK;
+}
+
+// Which kernels carry the fp16-copy path besides the bf16 one (both are
+// compiled into the kernel, so its registers are the larger path's).
+constexpr int F16_MAX_MB = 8;       // register and LDS variants: row blocks up to this
+constexpr bool F16_WIDE = true;     // the wide-M unit
+
+// End of a unit computed from the fp16 copy, in two steps around the
+// work-group barrier that follows the sums' write to LDS. f16_flag (every
+// wave, before the barrier): scales its sums back by 2^-ACT_F16_SHIFT (exact)
+// and records in the wave's own LDS word whether any of them is a NaN (every
+// wave writes its word for every unit, so nothing needs clearing).
+// f16_met_marker (after the barrier): whether any wave's sums held a NaN; the
+// unit must then be computed again from the bf16 copy. The words are read
+// before the next unit's barrier-separated writes.
+__device__ inline unsigned *f16_flags() {
+  static __shared__ unsigned s_f16bad[WG_WAVES];
+  return s_f16bad;
+}
+
+template <int R, int MB>
+__device__ inline void f16_flag(f32x4 (&acc)[R][MB], int wave, int lane) {
+  bool bad = false;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bad |= acc[r][mb][i] != acc[r][mb][i];
+      acc[r][mb] *= 1.0f / (float)(1 << ACT_F16_SHIFT);
+    }
+  const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
+  if (lane == 0) f16_flags()[wave] = any ? 1u : 0u;
+}
+
+__device__ inline bool f16_met_marker() {
+  const unsigned *f = f16_flags();
+  unsigned x = 0;
+#pragma unroll
+  for (int w = 0; w < WG_WAVES; ++w) x |= f[w];
+  return x != 0;
+}
+
 struct WTile {
   uint4 c[2];  // code halves
   uint32_t s;  // 4 scale bytes
@@ -84,8 +188,8 @@ __device__ inline void load_wtile(WTile &t, __amdgpu_buffer_rsrc_t rs, int kt, b
 
 // The 8 activation fragments of k-tile kt for each 16-row block (packed
 // activations); lanes whose row is >= M, or `ok` false, read zeros.
-template <int MB>
-__device__ inline void load_afrag(bf16x8 (&b)[MB][8], __amdgpu_buffer_rsrc_t ra, int kt, bool ok,
+template <int MB, class Frag>
+__device__ inline void load_afrag(Frag (&b)[MB][8], __amdgpu_buffer_rsrc_t ra, int kt, bool ok,
                                   int M, int lane) {
   const int col = lane & 15;
 #pragma unroll
@@ -100,27 +204,26 @@ __device__ inline void load_afrag(bf16x8 (&b)[MB][8], __amdgpu_buffer_rsrc_t ra,
   }
 }
 
-// Code half C of a weight tile (s: its four scales as fp32) into the MB
+// Code half C of a weight tile (dq: its dequantiser) into the MB
 // accumulators: 4 x (dequant 8 codes, MB MFMAs).
-template <int MB, int C>
-__device__ inline void compute_whalf(const WTile &t, const float (&s)[4], const bf16x8 (&b)[MB][8],
-                                     f32x4 (&acc)[MB]) {
+template <int MB, int C, bool F16>
+__device__ inline void compute_whalf(const WTile &t, const Dq<F16> &dq,
+                                     const typename Dq<F16>::frag (&b)[MB][8], f32x4 (&acc)[MB]) {
   const uint32_t cw[4] = {t.c[C].x, t.c[C].y, t.c[C].z, t.c[C].w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const bf16x8 wf = dequant8(cw[j], s[2 * C + (j >> 1)]);
+    const typename Dq<F16>::frag wf = dq(cw[j], 2 * C + (j >> 1));
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, b[mb][4 * C + j], acc[mb], 0, 0, 0);
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma(wf, b[mb][4 * C + j], acc[mb]);
   }
 }
 
-template <int MB>
-__device__ inline void compute_wtile(const WTile &t, const bf16x8 (&b)[MB][8], f32x4 (&acc)[MB]) {
-  float s[4];
-  scales4(t.s, s);
-  compute_whalf<MB, 0>(t, s, b, acc);
-  compute_whalf<MB, 1>(t, s, b, acc);
+template <int MB, bool F16>
+__device__ inline void compute_wtile(const WTile &t, const typename Dq<F16>::frag (&b)[MB][8],
+                                     f32x4 (&acc)[MB]) {
+  const Dq<F16> dq(t.s);
+  compute_whalf<MB, 0, F16>(t, dq, b, acc);
+  compute_whalf<MB, 1, F16>(t, dq, b, acc);
 }
 
 // compute_wtile followed by the tile's reload with k-tile kt, in two halves:
@@ -128,18 +231,18 @@ __device__ inline void compute_wtile(const WTile &t, const bf16x8 (&b)[MB][8], f
 // has been consumed, the second code half after the second. The register
 // variant's ring uses it (measured on MI355X: 2 % faster over the pass at
 // 1-8 rows, 1.7 % at 16); the LDS variant keeps compute then load.
-template <int MB>
-__device__ inline void compute_reload_wtile(WTile &t, const bf16x8 (&b)[MB][8], f32x4 (&acc)[MB],
-                                            __amdgpu_buffer_rsrc_t rs, int kt, bool ok, int lane) {
-  float s[4];
-  scales4(t.s, s);
+template <int MB, bool F16>
+__device__ inline void compute_reload_wtile(WTile &t, const typename Dq<F16>::frag (&b)[MB][8],
+                                            f32x4 (&acc)[MB], __amdgpu_buffer_rsrc_t rs, int kt, bool ok,
+                                            int lane) {
+  const Dq<F16> dq(t.s);
   const int base = ok ? kt * TILE_BYTES : OOB;
-  compute_whalf<MB, 0>(t, s, b, acc);
+  compute_whalf<MB, 0, F16>(t, dq, b, acc);
   const auto c0 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + lane * 16, 0, WEIGHT_AUX);
   const auto sc = __builtin_amdgcn_raw_buffer_load_b32(rs, base + SCALE_OFFSET + lane * 4, 0, WEIGHT_AUX);
   __builtin_memcpy(&t.c[0], &c0, 16);
   t.s = (uint32_t)sc;
-  compute_whalf<MB, 1>(t, s, b, acc);
+  compute_whalf<MB, 1, F16>(t, dq, b, acc);
   const auto c1 = __builtin_amdgcn_raw_buffer_load_b128(rs, base + CODE_HALF_BYTES + lane * 16, 0, WEIGHT_AUX);
   __builtin_memcpy(&t.c[1], &c1, 16);
 }
@@ -167,16 +270,26 @@ __device__ inline float glue_pair(float g, float u, float c) {
 }
 
 // Four consecutive bf16 outputs (column j, j % 4 == 0) of row m: into the next
-// GEMM's packed activations and the optional row-major copies.
+// GEMM's packed activations (both copies) and the optional row-major copies.
 __device__ inline void store_next(const Epilogue &epi, int mblocks, int m, int j, int cols,
                                   const float (&o)[4]) {
-  const uint32_t lo = (uint32_t)bf16_bits(o[0]) | ((uint32_t)bf16_bits(o[1]) << 16);
-  const uint32_t hi = (uint32_t)bf16_bits(o[2]) | ((uint32_t)bf16_bits(o[3]) << 16);
+  uint16_t b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = bf16_bits(o[i]);
+  const uint32_t lo = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+  const uint32_t hi = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
   const uint2 v = make_uint2(lo, hi);
-  // Write-through (system-coherent) store: a consumer on another die reads it
-  // through its own L2 without a write-back fence.
-  __hip_atomic_store(reinterpret_cast<uint64_t *>(epi.act + act_offset(m, j, mblocks)),
-                     (uint64_t)lo | ((uint64_t)hi << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  // Write-through (system-coherent) stores: a consumer on another die reads
+  // them through its own L2 without a write-back fence.
+  uint8_t *dst = epi.act + act_offset(m, j, mblocks);
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(dst), (uint64_t)lo | ((uint64_t)hi << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_SYSTEM);
+  if (epi.act16) {
+    const uint64_t h = (uint64_t)f16_act_bits(b[0]) | ((uint64_t)f16_act_bits(b[1]) << 16) |
+                       ((uint64_t)f16_act_bits(b[2]) << 32) | ((uint64_t)f16_act_bits(b[3]) << 48);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(dst + epi.act16), h, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
+  }
   if (epi.rm0) *reinterpret_cast<uint2 *>(epi.rm0 + (size_t)m * cols + j) = v;
   if (epi.rm1) *reinterpret_cast<uint2 *>(epi.rm1 + (size_t)m * cols + j) = v;
 }
@@ -256,8 +369,12 @@ __device__ inline void epilogue(const f32x4 *red, int nw, int tid, int M, int N,
 
 // Arguments of one GEMM (one phase of the pass, or one verify_gemm call).
 struct GemmArgs {
-  const uint8_t *act;  // packed activations
-  int M, act_bytes;
+  const uint8_t *act;  // packed activations (the bf16 copy)
+  int M, act_bytes;    // act_bytes: one copy
+  // > 0: the fp16 copy lies act16 bytes after `act`, and the units compute
+  // from it (computing a unit again from the bf16 copy where it meets a
+  // marker); 0: from the bf16 copy.
+  int act16 = 0;
   // M > 64 (the wide unit only): the rows come as two packed blocks, rows
   // 0..63 at `act` and rows 64.. at act + act_blk1 bytes (the layout
   // pack_activations writes for more than 64 rows).
@@ -465,10 +582,13 @@ __device__ inline void unit_tail(const GemmArgs &g, int rb, int ks, int ksplit, 
 // latency, not throughput, bounds the unit). `red` is the work-group's LDS
 // buffer of WG_WAVES * R * MB * 64 f32x4. Every thread of the work-group calls
 // this with the same arguments; it returns with the LDS buffer free for the
-// next unit.
-template <int MB, int R, int D, bool A2 = false>
-__device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int ks, int ksplit, f32x4 *red) {
-  const uint8_t *__restrict__ act = g.act;
+// next unit. F16: computes from the fp16 copy and returns false, before the
+// exchange and with nothing written, if the unit met a marker (the caller
+// then runs the unit with F16 false); else returns true.
+template <int MB, int R, int D, bool A2, bool F16>
+__device__ inline bool gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int ks, int ksplit, f32x4 *red) {
+  typedef typename Dq<F16>::frag Frag;
+  const uint8_t *__restrict__ act = g.act + (F16 ? g.act16 : 0);
   const int M = g.M, act_bytes = g.act_bytes, nrt = g.nrt, nkt = g.nkt;
   const uint8_t *__restrict__ W = g.W;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -506,7 +626,7 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
     // next one. For MB x R where two full rings do not fit in registers.
     static_assert(D == 1, "the two-deep activation ring goes with a one-deep weight ring");
     WTile w[R];
-    bf16x8 a[2][MB][8];
+    Frag a[2][MB][8];
     load_afrag<MB>(a[0], ra, kbeg, 0 < n, M, lane);
 #pragma unroll
     for (int r = 0; r < R; ++r) load_wtile(w[r], rs[r], kbeg, 0 < n, lane);
@@ -522,22 +642,24 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
       for (int d = 0; d < 2; ++d) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
-          compute_reload_wtile<MB>(w[r], a[d], acc[r], rs[r], kbeg + i + d + 1, i + d + 1 < n, lane);
+          compute_reload_wtile<MB, F16>(w[r], a[d], acc[r], rs[r], kbeg + i + d + 1, i + d + 1 < n, lane);
         load_afrag<MB>(a[d], ra, kbeg + i + d + 2, i + d + 2 < n, M, lane);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (i < n) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) compute_wtile<MB>(w[r], a[0], acc[r]);
+      for (int r = 0; r < R; ++r) compute_wtile<MB, F16>(w[r], a[0], acc[r]);
     }
+    if (F16) f16_flag(acc, wave, lane);
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
     __syncthreads();
+    if (F16 && f16_met_marker()) return false;
     unit_tail<MB, R, WG_WAVES>(g, rb, ks, ksplit, red, tid);
-    return;
+    return true;
   }
 
   // A ring of D k-tiles (weights and activation fragments) per wave: slot d
@@ -549,7 +671,7 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
   // D - 1 k-tiles in flight. The remaining k-tiles (fewer than D) are
   // computed after the loop without new loads.
   WTile w[D][R];
-  bf16x8 a[D][MB][8];
+  Frag a[D][MB][8];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     load_afrag<MB>(a[d], ra, kbeg + d, d < n, M, lane);
@@ -563,7 +685,7 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
     for (int d = 0; d < D; ++d) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        compute_reload_wtile<MB>(w[d][r], a[d], acc[r], rs[r], kbeg + i + d + D, i + d + D < n, lane);
+        compute_reload_wtile<MB, F16>(w[d][r], a[d], acc[r], rs[r], kbeg + i + d + D, i + d + D < n, lane);
       load_afrag<MB>(a[d], ra, kbeg + i + d + D, i + d + D < n, M, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -572,9 +694,10 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
   for (int d = 0; d < D - 1; ++d) {
     if (i + d < n) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) compute_wtile<MB>(w[d][r], a[d], acc[r]);
+      for (int r = 0; r < R; ++r) compute_wtile<MB, F16>(w[d][r], a[d], acc[r]);
     }
   }
+  if (F16) f16_flag(acc, wave, lane);
 
   // Sum the 4 waves' tiles in wave order (LDS), then either finish here
   // (ksplit == 1) or exchange partial tiles with the other splits.
@@ -583,7 +706,9 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
   __syncthreads();
+  if (F16 && f16_met_marker()) return false;
   unit_tail<MB, R, WG_WAVES>(g, rb, ks, ksplit, red, tid);
+  return true;
 }
 
 
@@ -596,8 +721,10 @@ __device__ inline void gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
 // across its R weight tiles. Weights stream through each wave's two-deep
 // register ring as in gemm_unit. One work-group barrier per k-tile.
 // `lds` holds 2 slots of MB * 8 KiB, then the RT tiles' sums and the ticket.
-template <int MB, int R>
-__device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t *lds) {
+// F16 and the result as in gemm_unit.
+template <int MB, int R, bool F16>
+__device__ inline bool gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t *lds) {
+  typedef typename Dq<F16>::frag Frag;
   constexpr int RT = WG_WAVES * R;
   constexpr int SLOT = MB * 8 * ACT_FRAG_BYTES;  // one k-tile of packed activations
   constexpr int PER_THREAD = SLOT / WG_THREADS / 16;  // 16-byte chunks per thread (2 MB)
@@ -616,8 +743,8 @@ __device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
     rs[r] = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, rt < nrt ? stripe_bytes : 0,
                                               RAW_BUFFER_FLAGS);
   }
-  const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc((void *)g.act, (short)0, g.act_bytes, RAW_BUFFER_FLAGS);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(g.act + (F16 ? g.act16 : 0)), (short)0, g.act_bytes, RAW_BUFFER_FLAGS);
   f32x4 *red = reinterpret_cast<f32x4 *>(lds + 2 * SLOT);
 
   // Staging: k-tile j's packed block is contiguous (SLOT bytes at j * SLOT);
@@ -635,7 +762,7 @@ __device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
 #pragma unroll
     for (int c = 0; c < PER_THREAD; ++c) dst[c * WG_THREADS + tid] = v[c];
   };
-  auto frags = [&](bf16x8 (&b)[MB][8], int slot) {
+  auto frags = [&](Frag (&b)[MB][8], int slot) {
     const uint4 *src = reinterpret_cast<const uint4 *>(lds + slot * SLOT);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -675,13 +802,13 @@ __device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
 #define NVFP4V_LDS_STEP(W, S_NEXT, SLOT_I)                                               \
   {                                                                                               \
     lds_barrier_wg();                                                                             \
-    bf16x8 b[MB][8];                                                                              \
+    Frag b[MB][8];                                                                                \
     frags(b, SLOT_I);                                                                             \
     stage_store(S_NEXT, 1 - SLOT_I);                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                            \
     stage_load(S_NEXT, i + 3);                                                                    \
     __builtin_amdgcn_sched_barrier(0);                                                            \
-    _Pragma("unroll") for (int r = 0; r < R; ++r) compute_wtile<MB>(W[r], b, acc[r]);            \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) compute_wtile<MB, F16>(W[r], b, acc[r]);       \
     __builtin_amdgcn_sched_barrier(0);                                                            \
     _Pragma("unroll") for (int r = 0; r < R; ++r) load_wtile(W[r], rs[r], kA + i + 2, i + 2 < n, lane); \
     __builtin_amdgcn_sched_barrier(0);                                                            \
@@ -698,13 +825,16 @@ __device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
 
   // Each wave's tiles into slice 0 of the sums (tile wave * R + r), then the
   // shared tail (split-K exchange, epilogue).
+  if (F16) f16_flag(acc, wave, lane);
   lds_barrier_wg();
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
   __syncthreads();
+  if (F16 && f16_met_marker()) return false;
   unit_tail<MB, RT, 1, true>(g, rb, ks, g.ksplit, red, tid);
+  return true;
 }
 
 // The wide-M unit (33..128 rows): like gemm_unit_lds, the 4 waves split N
@@ -718,8 +848,9 @@ __device__ inline void gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
 // second dequant is needed. One LDS slot: the next k-tile's activations wait
 // in registers (MB / 2 16-byte chunks per thread) until every wave has
 // finished reading the slot; two work-group barriers per k-tile.
-template <int MB, int R>
-__device__ inline void gemm_unit_wide(const GemmArgs &g, int rb, int ks, uint8_t *lds) {
+template <int MB, int R, bool F16>
+__device__ inline bool gemm_unit_wide(const GemmArgs &g, int rb, int ks, uint8_t *lds) {
+  typedef typename Dq<F16>::frag Frag;
   constexpr int RT = WG_WAVES * R;
   constexpr int SLOT = MB * 8 * ACT_FRAG_BYTES;       // one k-tile of packed activations
   constexpr int PER_THREAD = SLOT / WG_THREADS / 16;  // 16-byte chunks per thread
@@ -739,8 +870,8 @@ __device__ inline void gemm_unit_wide(const GemmArgs &g, int rb, int ks, uint8_t
     rs[r] = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, rt < nrt ? stripe_bytes : 0,
                                               RAW_BUFFER_FLAGS);
   }
-  const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc((void *)g.act, (short)0, g.act_bytes, RAW_BUFFER_FLAGS);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(g.act + (F16 ? g.act16 : 0)), (short)0, g.act_bytes, RAW_BUFFER_FLAGS);
 
   // The slot holds [row block][fragment q][lane]; thread t moves chunks
   // c * 256 + t, i.e. row block c / 2, second half of its fragments if c is
@@ -776,26 +907,26 @@ __device__ inline void gemm_unit_wide(const GemmArgs &g, int rb, int ks, uint8_t
   // Products of one k-tile: for each half C and group j of 8 codes, R
   // dequantised weight fragments against MB activation fragments.
   auto compute = [&](const WTile (&W)[R]) {
-    float sc[R][4];
+    Dq<F16> dq[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) scales4(W[r].s, sc[r]);
+    for (int r = 0; r < R; ++r) dq[r] = Dq<F16>(W[r].s);
 #pragma unroll
     for (int C = 0; C < 2; ++C)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bf16x8 wf[R];
+        Frag wf[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const uint32_t cw = j == 0 ? W[r].c[C].x : j == 1 ? W[r].c[C].y : j == 2 ? W[r].c[C].z : W[r].c[C].w;
-          wf[r] = dequant8(cw, sc[r][2 * C + (j >> 1)]);
+          wf[r] = dq[r](cw, 2 * C + (j >> 1));
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const uint4 x = afr[(mb * 8 + 4 * C + j) * 64 + lane];
-          bf16x8 b;
+          Frag b;
           __builtin_memcpy(&b, &x, 16);
 #pragma unroll
-          for (int r = 0; r < R; ++r) acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[r], b, acc[r][mb], 0, 0, 0);
+          for (int r = 0; r < R; ++r) acc[r][mb] = mfma(wf[r], b, acc[r][mb]);
         }
       }
   };
@@ -838,13 +969,16 @@ __device__ inline void gemm_unit_wide(const GemmArgs &g, int rb, int ks, uint8_t
   // The tiles' sums reuse the LDS (slice 0, tile wave * R + r), then the
   // shared tail (split-K exchange, epilogue).
   f32x4 *red = reinterpret_cast<f32x4 *>(lds);
+  if (F16) f16_flag(acc, wave, lane);
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) red[((wave * R + r) * MB + mb) * 64 + lane] = acc[r][mb];
   __syncthreads();
+  if (F16 && f16_met_marker()) return false;
   unit_tail<MB, RT, 1, true>(g, rb, ks, g.ksplit, red, tid);
+  return true;
 }
 
 }  // namespace dev

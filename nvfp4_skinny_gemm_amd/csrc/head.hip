@@ -350,7 +350,7 @@ int launch_head_block(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k,
   g.W = (const uint8_t *)packed;
   g.scales = (const float *)(g.W + (size_t)g.nrt * (size_t)g.nkt * HEAD_TILE_BYTES);
   g.act = act;
-  g.act_bytes = (int)act_packed_bytes(m, k);
+  g.act_bytes = (int)act_copy_bytes(m, k);
   g.C = c;
   g.M = (int)m;
   g.N = (int)n;
@@ -459,7 +459,7 @@ extern "C" int nvfp4v_fp8_head_gemm(nvfp4v_ctx *ctx, const uint16_t *a, int64_t 
   if (fault_injected()) return NVFP4V_E_FAULT;
   for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
     const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
-    rc = launch_pack_act(ctx, a + r0 * k, mc, k, ctx->act, stream);
+    rc = launch_pack_act(ctx, a + r0 * k, mc, k, ctx->act, 0, stream);  // the bf16 copy only
     if (!rc) rc = launch_head_block(ctx, ctx->act, mc, k, packed, n, c + r0 * n, stream);
   }
   return rc;

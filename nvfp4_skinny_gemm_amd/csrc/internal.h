@@ -47,10 +47,26 @@ struct Layout {
 // Activations in MFMA fragment order ("packed activations"): for k-tile kt,
 // 16-row block mb and fragment q = 0..7, a 1 KiB chunk at
 //   ((kt * MB + mb) * 8 + q) * 1024
-// whose lane L = col + 16 h holds 8 bf16: A[16 mb + col][256 kt + 64 h + 8 q + e],
+// whose lane L = col + 16 h holds 8 values A[16 mb + col][256 kt + 64 h + 8 q + e],
 // e = 0..7 (MB = ceil(M / 16)). A wave reads one fragment with one fully
 // coalesced 16-byte load per lane. Rows >= M are never read.
+//
+// The packed form holds two copies of A in this order: the bf16 values, and
+// `act16` bytes further on (the size of one copy) the same values as fp16
+// times 2^ACT_F16_SHIFT. A bf16 value converts to fp16 exactly when it is 0 or
+// its magnitude lies in [2^(-17-S), 2^(16-S)) (S = the shift; fp16 keeps all 8
+// significant bits there, as a normal or subnormal number); any other value
+// (too small or large, inf, NaN) is stored in the fp16 copy as the NaN
+// ACT_F16_MARK. The GEMM takes the fp16 copy: its products of exact fp16
+// weights and exact fp16 activations are the bf16 path's products times 2^S,
+// so the fp32 sums are too (measured on MI355X: v_mfma_f32_16x16x32_f16 and
+// _bf16 on the same values agree bitwise), and the sums are scaled back
+// exactly. A marker turns the sums it enters into NaN (NaN times zero is NaN
+// in both MFMAs), and a unit whose sums hold a NaN is computed again from the
+// bf16 copy, so every result equals the bf16 path's.
 constexpr int ACT_FRAG_BYTES = 1024;
+constexpr int ACT_F16_SHIFT = 8;
+constexpr uint16_t ACT_F16_MARK = 0x7FFF;
 
 // Words of the persistent pass's barrier block (context memory).
 constexpr int PASS_SYNC_WORDS = 1280;
@@ -61,16 +77,22 @@ constexpr int PASS_SYNC_WORDS = 1280;
 // its own row count; a GEMM over them runs once per block.
 constexpr int CHUNK_M = 64;
 
+// Bytes of one copy of one block of rows.
 inline size_t act_block_bytes(int64_t m, int64_t k) {
   const int64_t mb = (m + 15) / 16, nkt = (k + 255) / 256;
   return (size_t)nkt * (size_t)mb * 8 * ACT_FRAG_BYTES;
 }
 
-inline size_t act_packed_bytes(int64_t m, int64_t k) {
+// Bytes of one copy (all blocks of rows): the distance from the bf16 copy to
+// the fp16 copy of packed activations written for all m rows at once.
+inline size_t act_copy_bytes(int64_t m, int64_t k) {
   size_t total = 0;
   for (int64_t r0 = 0; r0 < m; r0 += CHUNK_M) total += act_block_bytes(m - r0 < CHUNK_M ? m - r0 : CHUNK_M, k);
   return total;
 }
+
+// Bytes of the packed form (both copies).
+inline size_t act_packed_bytes(int64_t m, int64_t k) { return 2 * act_copy_bytes(m, k); }
 
 // Byte offset of element (row, col) of A inside the packed activations.
 __host__ __device__ inline size_t act_offset(int64_t row, int64_t k, int mblocks) {
@@ -249,9 +271,11 @@ int make_plan(const nvfp4v_ctx *ctx, const Layout &L, int64_t m, Plan *p);
 int parse_tile_table(const char *text, TileRule *rules, int *n_rules);
 // Sets ctx->xcd_local from a dispatch probe (synchronous; at create).
 int probe_dispatch(nvfp4v_ctx *ctx);
-// Enqueue A (row-major bf16) -> packed activations (no argument checks).
+// Enqueue A (row-major bf16, at most CHUNK_M rows) -> packed activations (no
+// argument checks): the bf16 copy at `act` and, when act16 > 0, the fp16 copy
+// act16 bytes further on.
 int launch_pack_act(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
-                    hipStream_t stream, unsigned *sync = nullptr);
+                    size_t act16, hipStream_t stream, unsigned *sync = nullptr);
 // Fused epilogue of a GEMM in the chained pass: besides (optionally) writing
 // the fp32 C, turn C into the next GEMM's bf16 input, in packed-activation
 // order, and optionally into up to two row-major bf16 copies.
@@ -267,16 +291,25 @@ struct Epilogue {
   int col0 = 0, col1 = 0;
   float c = 1.f;
   uint8_t *act = nullptr;  // packed activations of the next GEMM (its K = out columns)
+  int act16 = 0;           // > 0: also write their fp16 copy, act16 bytes after `act`
   uint16_t *rm0 = nullptr, *rm1 = nullptr;  // optional row-major bf16 copies [M][out cols]
   int write_c = 1;
 };
-// Enqueue the GEMM on packed activations (no argument checks; m <= CHUNK_M).
-int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
-                int64_t n, float ts, float *c, hipStream_t stream, const Epilogue &epi = Epilogue());
-// The same for any m: one launch per block of CHUNK_M rows (plain epilogue).
+// Enqueue the GEMM on packed activations (no argument checks; m <= CHUNK_M,
+// or the wide unit's rows). act16 > 0: the fp16 copy lies act16 bytes after
+// `act` and the GEMM computes from it; 0: from the bf16 copy.
+int launch_gemm(nvfp4v_ctx *ctx, const uint8_t *act, size_t act16, int64_t m, int64_t k,
+                const void *packed, int64_t n, float ts, float *c, hipStream_t stream,
+                const Epilogue &epi = Epilogue());
+// The same for any m over activations packed by launch_pack_rows: one launch
+// per block of CHUNK_M rows, or one of the wide unit (plain epilogue).
 int launch_gemm_rows(nvfp4v_ctx *ctx, const uint8_t *act, int64_t m, int64_t k, const void *packed,
                      int64_t n, float ts, float *c, hipStream_t stream);
-// Row-major A of any m -> packed activations in blocks of CHUNK_M rows.
+// Row-major A of any m -> packed activations in blocks of CHUNK_M rows, both
+// copies (act_packed_bytes(m, k) bytes).
 int launch_pack_rows(nvfp4v_ctx *ctx, const uint16_t *a, int64_t m, int64_t k, uint8_t *act,
                      hipStream_t stream);
+// Whether the GEMMs compute from the fp16 copy (NVFP4V_F16=0: from the bf16
+// copy; both give the same C).
+bool use_f16();
 }  // namespace nvfp4v

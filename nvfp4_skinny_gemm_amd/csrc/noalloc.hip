@@ -23,7 +23,7 @@ namespace {
 constexpr size_t COUNTER_WORDS = 4096;
 constexpr size_t COUNTER_BYTES = COUNTER_WORDS * sizeof(unsigned);  // 16 KiB
 constexpr size_t ACT_OFFSET = 64 << 10;
-constexpr size_t ACT_CAP = size_t(8) << 20;       // packed activations of one 64-row block
+constexpr size_t ACT_CAP = size_t(16) << 20;      // packed activations of one 64-row block (both copies)
 constexpr size_t PART_OFFSET = ACT_OFFSET + ACT_CAP;
 constexpr size_t PART_CAP = size_t(8) << 20;      // split-K partial sums
 constexpr size_t SCRATCH_BYTES = PART_OFFSET + PART_CAP;
@@ -60,7 +60,7 @@ extern "C" int nvfp4v_verify_gemm_static(const uint16_t *a, int64_t m, int64_t k
   Layout L;
   if (!make_layout(n, k, &L)) return NVFP4V_E_SHAPE;
   if (!aligned16(a) || !aligned16(packed) || !aligned16(c)) return NVFP4V_E_ALIGN;
-  if (act_block_bytes(std::min<int64_t>(m, CHUNK_M), k) > ACT_CAP) return NVFP4V_E_WORKSPACE;
+  if (2 * act_block_bytes(std::min<int64_t>(m, CHUNK_M), k) > ACT_CAP) return NVFP4V_E_WORKSPACE;
   // A context on the stack (no allocation) whose workspace is the scratch
   // array: built-in tile table, exchange through memory.
   nvfp4v_ctx local;
@@ -93,10 +93,12 @@ extern "C" int nvfp4v_verify_gemm_static(const uint16_t *a, int64_t m, int64_t k
   // the call can be captured in a graph).
   hipLaunchKernelGGL(k_clear_counters, dim3(16), dim3(256), 0, stream, local.counters, (int)COUNTER_WORDS);
   int rc = hip_status(&local, hipGetLastError());
+  const bool f16 = use_f16();
   for (int64_t r0 = 0; r0 < m && rc == NVFP4V_OK; r0 += CHUNK_M) {
     const int64_t mc = std::min<int64_t>(CHUNK_M, m - r0);
-    rc = launch_pack_act(&local, a + r0 * k, mc, k, local.act, stream);
-    if (!rc) rc = launch_gemm(&local, local.act, mc, k, packed, n, ts, c + r0 * n, stream);
+    const size_t act16 = act_block_bytes(mc, k);
+    rc = launch_pack_act(&local, a + r0 * k, mc, k, local.act, act16, stream);
+    if (!rc) rc = launch_gemm(&local, local.act, f16 ? act16 : 0, mc, k, packed, n, ts, c + r0 * n, stream);
   }
   return rc;
 }

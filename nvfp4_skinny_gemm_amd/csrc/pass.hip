@@ -80,15 +80,16 @@ __global__ void k_glue_sum(const float *__restrict__ x, int64_t ldx, const float
 }
 
 // Zero the last k-tile of the packed-activation blocks whose K is not a
-// multiple of 256, for every layer (and the block after the last layer): the
-// epilogues write only the columns below K, while the GEMMs read whole k-tiles
-// (the padded weights there are zero, but zero times a stale NaN is not).
-// Block (l, j) starts at l * stride + off[j]; its tail is `tail[j]` bytes at
-// tail_off[j] within it (tail[j] == 0: nothing to zero).
+// multiple of 256, for every layer (and the block after the last layer), in
+// both copies: the epilogues write only the columns below K, while the GEMMs
+// read whole k-tiles (the padded weights there are zero, but zero times a
+// stale NaN is not). Block (l, j) starts at l * stride + off[j], its fp16 copy
+// act16[j] bytes later; the tail is `tail[j]` bytes at tail_off[j] within a
+// copy (tail[j] == 0: nothing to zero).
 struct TailArgs {
   uint8_t *act0;
   size_t stride;
-  size_t off[4], tail_off[4];
+  size_t off[4], tail_off[4], act16[4];
   int tail[4];
   int layers;  // blocks of layers 0..layers-1 (all four), then block 0 of layer `layers`
 };
@@ -97,9 +98,13 @@ __global__ void k_zero_tails(TailArgs t) {
   const int l = blockIdx.y, j = blockIdx.z;
   if (l == t.layers && j != 0) return;
   const int n16 = t.tail[j] / 16;
-  uint4 *dst = reinterpret_cast<uint4 *>(t.act0 + (size_t)l * t.stride + t.off[j] + t.tail_off[j]);
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x)
+  uint8_t *blk = t.act0 + (size_t)l * t.stride + t.off[j] + t.tail_off[j];
+  uint4 *dst = reinterpret_cast<uint4 *>(blk);
+  uint4 *dst16 = reinterpret_cast<uint4 *>(blk + t.act16[j]);
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x) {
     dst[i] = make_uint4(0u, 0u, 0u, 0u);
+    dst16[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
 }
 
 unsigned glue_grid(int64_t total) {
@@ -377,7 +382,7 @@ void k_pass(PassArgs a) {
 // on zeros and neither flushes nor crosses.
 #define NVFP4V_PASS_STEP(W, A, WO, AO)                                                       \
   {                                                                                           \
-    _Pragma("unroll") for (int r = 0; r < R; ++r) compute_wtile<MB>(W[r], A, acc[r]);        \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) compute_wtile<MB, false>(W[r], A, acc[r]); \
     if (it0.p < np && last_of_task(it0)) {                                                    \
       flush_task<MB, R>(a, it0, acc, lds + (nflush & 1) * RED, words, tid, lane, wave);      \
       ++nflush;                                                                               \
@@ -479,7 +484,11 @@ int chain_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_
   const float ch = (float)(1.0 / std::sqrt((double)H));
   const float c2h = (float)(1.0 / std::sqrt(2.0 * (double)H));
   const float ci = (float)(1.0 / std::sqrt((double)I));
-  int rc = launch_pack_act(ctx, h0, m, H, w.act0, stream);
+  // The GEMMs compute from the fp16 copies (unless NVFP4V_F16=0), which the
+  // packing kernel and the epilogues write beside the bf16 ones.
+  const bool f16 = use_f16();
+  const size_t x16[4] = {f16 ? w.act16[0] : 0, f16 ? w.act16[1] : 0, f16 ? w.act16[2] : 0, f16 ? w.act16[3] : 0};
+  int rc = launch_pack_act(ctx, h0, m, H, w.act0, x16[0], stream);
   for (int l = 0; l < n_layers && rc == NVFP4V_OK; ++l) {
     const nvfp4v_layer &L = layers[l];
     uint8_t *blk = w.act0 + (size_t)l * w.layer_stride;
@@ -491,14 +500,15 @@ int chain_pass(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_layers, int64_
     e_g.mode = EPI_SCALE, e_g.col0 = 0, e_g.col1 = (int)H, e_g.c = ch, e_g.act = a_g;
     e_d.mode = EPI_PAIR, e_d.c = c2h, e_d.act = a_d;
     e_h.mode = EPI_SCALE, e_h.col0 = 0, e_h.col1 = (int)H, e_h.c = ci, e_h.act = a_next;
+    e_o.act16 = (int)x16[1], e_g.act16 = (int)x16[2], e_d.act16 = (int)x16[3], e_h.act16 = (int)x16[0];
     e_h.rm0 = (l == n_layers - 1) ? h_out : nullptr;
     e_h.rm1 = trace ? trace + (size_t)l * w.trace_m * H : nullptr;
     // Only the last layer's fp32 outputs are kept: earlier ones would be overwritten unread.
     e_o.write_c = e_g.write_c = e_d.write_c = e_h.write_c = (l == n_layers - 1) ? 1 : 0;
-    rc = launch_gemm(ctx, a_h, m, H, (const uint8_t *)L.qkv, 3 * H, L.ts_qkv, w.C[0], stream, e_o);
-    if (!rc) rc = launch_gemm(ctx, a_o, m, H, (const uint8_t *)L.o, H, L.ts_o, w.C[1], stream, e_g);
-    if (!rc) rc = launch_gemm(ctx, a_g, m, H, (const uint8_t *)L.gate_up, 2 * I, L.ts_gate_up, w.C[2], stream, e_d);
-    if (!rc) rc = launch_gemm(ctx, a_d, m, I, (const uint8_t *)L.down, H, L.ts_down, w.C[3], stream, e_h);
+    rc = launch_gemm(ctx, a_h, x16[0], m, H, (const uint8_t *)L.qkv, 3 * H, L.ts_qkv, w.C[0], stream, e_o);
+    if (!rc) rc = launch_gemm(ctx, a_o, x16[1], m, H, (const uint8_t *)L.o, H, L.ts_o, w.C[1], stream, e_g);
+    if (!rc) rc = launch_gemm(ctx, a_g, x16[2], m, H, (const uint8_t *)L.gate_up, 2 * I, L.ts_gate_up, w.C[2], stream, e_d);
+    if (!rc) rc = launch_gemm(ctx, a_d, x16[3], m, I, (const uint8_t *)L.down, H, L.ts_down, w.C[3], stream, e_h);
   }
   return rc;
 }
@@ -616,6 +626,7 @@ static int verify_pass_block(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_
     for (int j = 0; j < 4; ++j) {
       const int64_t nkt = (ks[j] + K_PER_TILE - 1) / K_PER_TILE;
       t.off[j] = w.act_off[j];
+      t.act16[j] = w.act16[j];
       t.tail_off[j] = (size_t)(nkt - 1) * mb * 8 * ACT_FRAG_BYTES;
       t.tail[j] = ks[j] % K_PER_TILE ? mb * 8 * ACT_FRAG_BYTES : 0;
       most = std::max(most, t.tail[j]);
@@ -678,7 +689,8 @@ static int verify_pass_block(nvfp4v_ctx *ctx, const nvfp4v_layer *layers, int n_
   ctx->last_pass_phases = 4 * n_layers;
   if (fault_injected()) return NVFP4V_E_FAULT;
 
-  int rc = launch_pack_act(ctx, h0, m, hidden, w.act0, stream, ctx->pass_sync);
+  // The persistent kernel computes from the bf16 copies only.
+  int rc = launch_pack_act(ctx, h0, m, hidden, w.act0, 0, stream, ctx->pass_sync);
   for (int l0 = 0; l0 < n_layers && rc == NVFP4V_OK; l0 += LAYERS_PER_LAUNCH) {
     a.layer0 = l0;
     a.n_layers = std::min(LAYERS_PER_LAUNCH, n_layers - l0);

@@ -19,14 +19,16 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ---------------------------------------------------------------------------
 // Workspace: the fp32 outputs of one layer (the last layer's are kept), then one
 // block of packed activations per layer and phase (each phase reads a buffer
-// of its own), then the packed h of the layer after the last one.
+// of its own), then the packed h of the layer after the last one. Each block
+// holds the bf16 copy and, act16 bytes after it, the fp16 copy.
 // ---------------------------------------------------------------------------
 struct PassWs {
   float *C[4];          // qkv [M][3H], o [M][H], gu [M][2I], d [M][H]
   uint8_t *act0;        // packed activations of layer 0, phase 0
   size_t layer_stride;  // bytes between the activation blocks of two layers
   size_t act_off[4];    // offset of phase j's input within a layer's block
-  size_t act_bytes[4];
+  size_t act_bytes[4];  // one copy
+  size_t act16[4];      // from the bf16 copy to the fp16 copy
   int64_t trace_m;      // rows of the trace's [layer][rows][H] layout (the pass's M, or
                         // the whole call's M when this pass is one block of its rows)
 };
@@ -42,18 +44,19 @@ inline size_t pass_ws_layout(int64_t m, int64_t H, int64_t I, int n_layers, uint
   w->C[1] = (float *)take((size_t)m * H * 4);
   w->C[2] = (float *)take((size_t)m * 2 * I * 4);
   w->C[3] = (float *)take((size_t)m * H * 4);
-  w->act_bytes[0] = act_packed_bytes(m, H);  // h
-  w->act_bytes[1] = act_packed_bytes(m, H);  // o_in
-  w->act_bytes[2] = act_packed_bytes(m, H);  // g_in
-  w->act_bytes[3] = act_packed_bytes(m, I);  // d_in
+  w->act_bytes[0] = act_copy_bytes(m, H);  // h
+  w->act_bytes[1] = act_copy_bytes(m, H);  // o_in
+  w->act_bytes[2] = act_copy_bytes(m, H);  // g_in
+  w->act_bytes[3] = act_copy_bytes(m, I);  // d_in
   size_t stride = 0;
   for (int j = 0; j < 4; ++j) {
     w->act_off[j] = stride;
-    stride += align256(w->act_bytes[j]);
+    w->act16[j] = align256(w->act_bytes[j]);
+    stride += 2 * w->act16[j];
   }
   w->layer_stride = stride;
   w->act0 = base ? base + off : nullptr;
-  off += stride * (size_t)n_layers + align256(w->act_bytes[0]);
+  off += stride * (size_t)n_layers + 2 * w->act16[0];
   w->trace_m = m;
   return off;
 }

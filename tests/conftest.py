@@ -36,3 +36,16 @@ def read_golden(name):
             key, *vals = line.split()
             rows[key] = vals
     return rows
+
+
+def f16_copy_expected(bits):
+    """What the packed activations' fp16 copy holds for bf16 values `bits`
+    (uint16): the value times 2^8 as fp16 where that is exact, else the NaN
+    marker 0x7FFF (the library's packed-activation layout)."""
+    import numpy as np
+
+    a = (bits.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        h = (a * np.float32(256)).astype(np.float16)
+        exact = h.astype(np.float32) / np.float32(256) == a
+    return np.where(exact, h.view(np.uint16), np.uint16(0x7FFF)).astype(np.uint16)

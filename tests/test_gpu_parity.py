@@ -10,6 +10,7 @@ import pytest
 
 import nvfp4_skinny_gemm_amd as nv
 import synth
+from conftest import f16_copy_expected
 
 pytestmark = pytest.mark.gpu
 
@@ -435,3 +436,102 @@ def test_splitk_exchange_paths_agree(torch_cuda, ctx, monkeypatch, plan):
         assert ctx_mem.device_status() == 0
     finally:
         ctx_mem.close()
+
+
+# bf16 values around the fp16 copy's exact range [2^-25, 2^8) (times 2^8:
+# fp16 normals and subnormals down to 2^-24) and outside it.
+def bf16_bits(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+SPECIAL_ACT = bf16_bits([2.0 ** -25, -2.0 ** -25, 2.0 ** -26, 3 * 2.0 ** -26, 1e-12, 255.0, -255.0, 256.0,
+                         1e5, -1e6, 0.0, -0.0, 2.0 ** -14, 1.5 * 2.0 ** -20, 2.0 ** -100])
+SPECIAL_BITS = np.concatenate([SPECIAL_ACT, np.array([0x0001, 0x8003, 0x7F80, 0xFF80, 0x7FC0], np.uint16)])
+
+
+def planted_activations(m, k, seed, bits, per_row=3):
+    """Synthetic bf16 activations [m, k] with `per_row` entries of each row
+    replaced by values drawn from `bits` (fixed positions per seed)."""
+    a = synth.activations_bf16(m, k, seed=seed, outliers=True).copy()
+    g = np.random.default_rng(seed + 1000)
+    for r in range(m):
+        cols = g.choice(k, per_row, replace=False)
+        a[r, cols] = g.choice(bits, per_row)
+    return a
+
+
+def unpack_block(buf, m, k):
+    """One block of at most 64 rows of packed activations (one copy) -> [m, k] uint16."""
+    mb = (m + 15) // 16
+    rows = np.arange(m)[:, None]
+    ks = np.arange(k)[None, :]
+    kt, rem = ks >> 8, ks & 255
+    h, q, e = rem >> 6, (rem >> 3) & 7, rem & 7
+    off = ((kt * mb + (rows >> 4)) * 8 + q) * 1024 + ((rows & 15) + 16 * h) * 16 + 2 * e
+    return buf.view(np.uint16)[off // 2]
+
+
+@pytest.mark.parametrize("m,k", [(1, 256), (16, 4112), (33, 1040), (64, 5120), (100, 2064)])
+def test_packed_activations_hold_both_copies(torch_cuda, ctx, m, k):
+    """pack_activations writes the bf16 values in fragment order and, one copy
+    further on, each value times 2^8 as fp16 where that is exact, else the
+    NaN marker (values planted at and beyond both ends of the exact range,
+    bf16 subnormals, infinities and NaN; ragged K and rows; two 64-row blocks
+    at M = 100)."""
+    torch = torch_cuda
+    a = planted_activations(m, k, seed=m + k, bits=SPECIAL_BITS)
+    act = ctx.pack_activations(bf16_dev(torch, a)).cpu().numpy()
+    assert act.size == nv.act_packed_bytes(m, k)
+    copy = act.size // 2
+    r0, off = 0, 0
+    while r0 < m:
+        mc = min(64, m - r0)
+        blk = ((k + 255) // 256) * ((mc + 15) // 16) * 8 * 1024
+        got = unpack_block(act[off:off + blk], mc, k)
+        got16 = unpack_block(act[copy + off:copy + off + blk], mc, k)
+        assert np.array_equal(got, a[r0:r0 + mc]), (m, k, r0)
+        assert np.array_equal(got16, f16_copy_expected(a[r0:r0 + mc])), (m, k, r0)
+        r0, off = r0 + mc, off + blk
+
+
+FP16_PLANS = ["r=1,ks=1", "r=2,ks=3", "r=4,ks=2", "r=8,ks=1", "r=2,ks=1,d=4", "r=4,ks=2,d=3",
+              "n:r=1,ks=1", "n:r=2,ks=5", "n:r=1,ks=18", "w:r=2,ks=3", "w:r=4,ks=2", "table"]
+
+
+@pytest.mark.parametrize("plan", FP16_PLANS)
+def test_fp16_copy_gives_bf16_results(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
+    """Every variant computing from the fp16 copy gives the C of the bf16 copy
+    (NVFP4V_F16=0) bitwise, on plain activations and on activations with a
+    marker in every row (values outside the fp16 copy's exact range: the unit
+    is computed again from the bf16 copy), and agrees with the oracle; with
+    NaN and infinite activations the NaN outputs fall in the same places."""
+    torch = torch_cuda
+    n, k = 272, 4608   # 17 row tiles (ragged for R = 2, 4, 8), 18 k-tiles
+    g = np.random.default_rng(53)
+    codes, scales = random_codes_scales(g, n, k)
+    packed = pack_dev(torch, ctx, codes, scales, n, k)
+    plain = synth.activations_bf16(128, k, seed=17, outliers=True)
+    marked = planted_activations(128, k, seed=19, bits=SPECIAL_ACT)
+    nonfinite = planted_activations(128, k, seed=23, bits=SPECIAL_BITS, per_row=1)
+    if plan != "table":
+        monkeypatch.setenv("NVFP4V_PLAN", plan)
+    if plan.startswith("w:"):
+        ms = (64, 128) if "r=4" in plan else (33, 48, 64, 65, 128)
+    else:
+        ms = (1, 16, 17, 33, 64) if plan.startswith("n:") or "r=8" not in plan else (1, 16, 33, 64)
+    for name, a in (("plain", plain), ("marked", marked), ("nonfinite", nonfinite)):
+        c_ref, s_ref = oracle_mod.gemm(a, codes, scales, ts=1.5) if name != "nonfinite" else (None, None)
+        a_dev = bf16_dev(torch, a)
+        for m in ms:
+            log("fp16 copy, plan %s, %s, M=%d: %s" % (plan, name, m, ctx.describe_plan(n, k, m)))
+            c16 = ctx.verify_gemm(a_dev[:m].contiguous(), packed, n, k, ts=1.5)
+            monkeypatch.setenv("NVFP4V_F16", "0")
+            cbf = ctx.verify_gemm(a_dev[:m].contiguous(), packed, n, k, ts=1.5)
+            monkeypatch.delenv("NVFP4V_F16")
+            torch.cuda.synchronize()
+            x16, xbf = c16.cpu().numpy(), cbf.cpu().numpy()
+            assert np.array_equal(np.isnan(x16), np.isnan(xbf)), (plan, name, m)
+            fin = ~np.isnan(x16)
+            assert np.array_equal(x16[fin].view(np.uint32), xbf[fin].view(np.uint32)), (plan, name, m)
+            if c_ref is not None:
+                assert_parity(oracle_mod, x16, c_ref[:m], s_ref[:m], "fp16 copy %s %s M=%d" % (plan, name, m))

@@ -16,6 +16,7 @@ import pytest
 
 import nvfp4_skinny_gemm_amd as nv
 import synth
+from conftest import f16_copy_expected
 
 pytestmark = pytest.mark.gpu
 
@@ -265,22 +266,25 @@ def unpack_act(buf, m, k):
 
 
 def workspace_views(ws, m, H, I, L):
-    """fp32 outputs of the last layer and each layer's packed input blocks."""
+    """fp32 outputs of the last layer and each layer's packed input blocks:
+    (bf16 copy, fp16 copy) per block."""
     sizes = [m * 3 * H * 4, m * H * 4, m * 2 * I * 4, m * H * 4]
     C, off = [], 0
     for sz in sizes:
         C.append(ws[off:off + sz].view(np.float32))
         off += align256(sz)
     act_bytes = [act_packed_bytes(m, H)] * 3 + [act_packed_bytes(m, I)]
-    stride = sum(align256(b) for b in act_bytes)
-    acts = []
+    stride = sum(2 * align256(b) for b in act_bytes)
+    acts, acts16 = [], []
     for l in range(L + 1):
-        blk, o = [], off + l * stride
+        blk, blk16, o = [], [], off + l * stride
         for b in act_bytes:
             blk.append(ws[o:o + b])
-            o += align256(b)
+            blk16.append(ws[o + align256(b):o + align256(b) + b])
+            o += 2 * align256(b)
         acts.append(blk)
-    return C, acts
+        acts16.append(blk16)
+    return C, acts, acts16
 
 
 @pytest.mark.parametrize("mode_ctx", MODES, indirect=True)
@@ -313,10 +317,19 @@ def run_and_check_last_layer(torch, ctx, oracle_mod, m, H, I, L, seed, sample):
     assert ctx.pass_status() == nv.OK, "pass gave up at site %d" % ctx.pass_error_site()
     torch.cuda.synchronize()
     assert torch.isfinite(trace.float()).all(), "non-finite activations in the pass"
-    C, acts = workspace_views(ws.cpu().numpy(), m, H, I, L)
+    C, acts, acts16 = workspace_views(ws.cpu().numpy(), m, H, I, L)
     for j in range(4):
         assert np.isfinite(C[j]).all(), "non-finite fp32 output of GEMM %d" % j
     last = L - 1
+    if ctx.get_pass_mode() == nv.PASS_CHAIN:
+        # the chained launches compute from the fp16 copies the packing kernel
+        # and the epilogues write beside the bf16 ones
+        for l in range(L + 1):
+            for j, kk in enumerate((H, H, H, I)):
+                if l == L and j:
+                    break
+                assert np.array_equal(unpack_act(acts16[l][j], m, kk),
+                                      f16_copy_expected(unpack_act(acts[l][j], m, kk))), (l, j)
     h_in = unpack_act(acts[last][0], m, H)
     assert np.array_equal(unpack_act(acts[0][0], m, H), a0[:m].view(np.uint16))
     if L > 1:

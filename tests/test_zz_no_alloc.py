@@ -61,5 +61,5 @@ def test_static_entry_argument_errors(torch_cuda):
     assert lib.nvfp4v_verify_gemm_static(p(a), 129, 256, p(packed), 32, 1.0, p(out), None) == nv.E_M_RANGE
     assert lib.nvfp4v_verify_gemm_static(p(a), 4, 250, p(packed), 32, 1.0, p(out), None) == nv.E_SHAPE
     assert lib.nvfp4v_verify_gemm_static(None, 4, 256, p(packed), 32, 1.0, p(out), None) == nv.E_INVALID_ARG
-    # K beyond the scratch array's activation block (8 MiB at 64 rows)
+    # K beyond the scratch array's activation block (16 MiB for both copies at 64 rows)
     assert lib.nvfp4v_verify_gemm_static(p(a), 64, 65536 + 256, p(packed), 32, 1.0, p(out), None) == nv.E_WORKSPACE
