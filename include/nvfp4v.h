@@ -120,6 +120,14 @@ int nvfp4v_load_tile_table(nvfp4v_ctx *ctx, const char *path);
  * Errors: INVALID_ARG, HIP. */
 int nvfp4v_device_status(nvfp4v_ctx *ctx);
 
+/* Synchronise the device, then write to *units_host the number of GEMM work
+ * units on this context that met a marker in the fp16 copy of their packed
+ * activations and were computed again from the bf16 copy (see
+ * nvfp4v_act_packed_bytes), counted since the context was created or last
+ * reported NVFP4V_E_DISPATCH. A measurement: with O(1) activations only values
+ * below 2^-25 in magnitude cause it. Errors: INVALID_ARG, HIP. */
+int nvfp4v_f16_redone(nvfp4v_ctx *ctx, uint64_t *units_host);
+
 /* Size in bytes of the opaque context object. Host-only tests use it to build a
  * zeroed stand-in context whose every argument check runs on the host and
  * returns before any HIP call (an all-zero context has an empty workspace). */

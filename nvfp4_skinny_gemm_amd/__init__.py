@@ -65,6 +65,7 @@ def load():
     lib.nvfp4v_ctx_size.argtypes = []
     lib.nvfp4v_ctx_size.restype = c.c_size_t
     lib.nvfp4v_device_status.argtypes = [p]
+    lib.nvfp4v_f16_redone.argtypes = [p, c.POINTER(c.c_uint64)]
     lib.nvfp4v_quantize_host.argtypes = [p, i64, i64, p, p]
     lib.nvfp4v_quantize.argtypes = [p, p, i64, i64, p, p, p]
     lib.nvfp4v_encode_e4m3_host.argtypes = [p, i64, p]
@@ -341,6 +342,12 @@ class Context:
     def device_status(self) -> int:
         """Synchronise; E_DISPATCH if some split-K row block's pieces ran on two XCDs, else 0."""
         return int(load().nvfp4v_device_status(self._h))
+
+    def f16_redone(self) -> int:
+        """Synchronise; GEMM work units computed again from the bf16 copy of their activations."""
+        n = ctypes.c_uint64(0)
+        _check(load().nvfp4v_f16_redone(self._h, ctypes.byref(n)), "nvfp4v_f16_redone")
+        return int(n.value)
 
     def last_hip_error(self) -> int:
         return int(load().nvfp4v_last_hip_error(self._h))

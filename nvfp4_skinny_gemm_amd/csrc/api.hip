@@ -116,6 +116,19 @@ extern "C" int nvfp4v_device_status(nvfp4v_ctx *ctx) {
   return NVFP4V_E_DISPATCH;
 }
 
+extern "C" int nvfp4v_f16_redone(nvfp4v_ctx *ctx, uint64_t *units) {
+  if (!ctx || !units) return NVFP4V_E_INVALID_ARG;
+  hipError_t e = hipSetDevice(ctx->device);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  unsigned w[DEV_STATUS_BYTES / sizeof(unsigned)];
+  if (e == hipSuccess) e = hipMemcpy(w, ctx->dev_status, DEV_STATUS_BYTES, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_status(ctx, e);
+  uint64_t n = 0;
+  for (int x = 0; x < 8; ++x) n += w[x * DEV_LINE_WORDS + DEV_F16_REDONE];
+  *units = n;
+  return NVFP4V_OK;
+}
+
 extern "C" size_t nvfp4v_ctx_size(void) { return sizeof(nvfp4v_ctx); }
 
 extern "C" int nvfp4v_last_hip_error(const nvfp4v_ctx *ctx) { return ctx ? ctx->last_hip : 0; }

@@ -73,8 +73,10 @@ void k_gemm(GemmArgs g) {
   if ((int)blockIdx.x >= g.nrb) return;  // grid padding
   if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
   const int ks = blockIdx.y, kA = ks * g.kts_per_split, kB = min(g.nkt, kA + g.kts_per_split);
-  if constexpr (MB <= F16_MAX_MB)
+  if constexpr (MB <= F16_MAX_MB) {
     if (g.act16 && gemm_unit<MB, R, D, A2, true>(g, blockIdx.x, kA, kB, ks, g.ksplit, red)) return;
+    count_f16_redone(g);
+  }
   gemm_unit<MB, R, D, A2, false>(g, blockIdx.x, kA, kB, ks, g.ksplit, red);
 }
 
@@ -89,8 +91,10 @@ void k_gemm_lds(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
   if ((int)blockIdx.x >= g.nrb) return;  // grid padding
   if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
-  if constexpr (MB <= F16_MAX_MB)
+  if constexpr (MB <= F16_MAX_MB) {
     if (g.act16 && gemm_unit_lds<MB, R, true>(g, blockIdx.x, blockIdx.y, lds)) return;
+    count_f16_redone(g);
+  }
   gemm_unit_lds<MB, R, false>(g, blockIdx.x, blockIdx.y, lds);
 }
 
@@ -101,8 +105,10 @@ void k_gemm_wide(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
   if ((int)blockIdx.x >= g.nrb) return;  // grid padding
   if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
-  if constexpr (F16_WIDE)
+  if constexpr (F16_WIDE) {
     if (g.act16 && gemm_unit_wide<MB, R, true>(g, blockIdx.x, blockIdx.y, lds)) return;
+    count_f16_redone(g);
+  }
   gemm_unit_wide<MB, R, false>(g, blockIdx.x, blockIdx.y, lds);
 }
 

@@ -137,8 +137,11 @@ constexpr bool F16_WIDE = true;     // the wide-M unit
 // End of a unit computed from the fp16 copy, in two steps around the
 // work-group barrier that follows the sums' write to LDS. f16_flag (every
 // wave, before the barrier): scales its sums back by 2^-ACT_F16_SHIFT (exact)
-// and records in the wave's own LDS word whether any of them is a NaN (every
-// wave writes its word for every unit, so nothing needs clearing).
+// and records in the wave's own LDS word whether any of them in a column
+// below M is a NaN (every wave writes its word for every unit, so nothing
+// needs clearing). Columns >= M are never stored, and the staged variants
+// read whatever the buffer holds in those padding rows, so a NaN there must
+// not send the unit to the bf16 path.
 // f16_met_marker (after the barrier): whether any wave's sums held a NaN; the
 // unit must then be computed again from the bf16 copy. The words are read
 // before the next unit's barrier-separated writes.
@@ -148,14 +151,15 @@ __device__ inline unsigned *f16_flags() {
 }
 
 template <int R, int MB>
-__device__ inline void f16_flag(f32x4 (&acc)[R][MB], int wave, int lane) {
+__device__ inline void f16_flag(f32x4 (&acc)[R][MB], int M, int wave, int lane) {
   bool bad = false;
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      const bool live = mb * 16 + (lane & 15) < M;  // this lane's column (row of A)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bad |= acc[r][mb][i] != acc[r][mb][i];
+      for (int i = 0; i < 4; ++i) bad |= live && acc[r][mb][i] != acc[r][mb][i];
       acc[r][mb] *= 1.0f / (float)(1 << ACT_F16_SHIFT);
     }
   const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
@@ -408,6 +412,12 @@ __device__ inline void count_row_block(unsigned *status, int which) {
   __hip_atomic_fetch_add(status + x * DEV_LINE_WORDS + which, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// A unit that computed from the fp16 copy and met a marker (called between
+// its fp16 and bf16 runs): counted in the context's status lines, if any.
+__device__ inline void count_f16_redone(const GemmArgs &g) {
+  if (g.act16 && g.status && threadIdx.x == 0) count_row_block(g.status, DEV_F16_REDONE);
+}
+
 // End of a work unit whose RT row tiles' sums sit in LDS: red[((w * RT + r) *
 // MB + mb) * 64 + lane] for slices w < NW (summed in slice order). The unit is
 // piece `ks` of the `ksplit` pieces (consecutive k-ranges, in k order) its row
@@ -651,7 +661,7 @@ __device__ inline bool gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
 #pragma unroll
       for (int r = 0; r < R; ++r) compute_wtile<MB, F16>(w[r], a[0], acc[r]);
     }
-    if (F16) f16_flag(acc, wave, lane);
+    if (F16) f16_flag(acc, g.M, wave, lane);
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -697,7 +707,7 @@ __device__ inline bool gemm_unit(const GemmArgs &g, int rb, int kA, int kB, int 
       for (int r = 0; r < R; ++r) compute_wtile<MB, F16>(w[d][r], a[d], acc[r]);
     }
   }
-  if (F16) f16_flag(acc, wave, lane);
+  if (F16) f16_flag(acc, g.M, wave, lane);
 
   // Sum the 4 waves' tiles in wave order (LDS), then either finish here
   // (ksplit == 1) or exchange partial tiles with the other splits.
@@ -825,7 +835,7 @@ __device__ inline bool gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
 
   // Each wave's tiles into slice 0 of the sums (tile wave * R + r), then the
   // shared tail (split-K exchange, epilogue).
-  if (F16) f16_flag(acc, wave, lane);
+  if (F16) f16_flag(acc, g.M, wave, lane);
   lds_barrier_wg();
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -969,7 +979,7 @@ __device__ inline bool gemm_unit_wide(const GemmArgs &g, int rb, int ks, uint8_t
   // The tiles' sums reuse the LDS (slice 0, tile wave * R + r), then the
   // shared tail (split-K exchange, epilogue).
   f32x4 *red = reinterpret_cast<f32x4 *>(lds);
-  if (F16) f16_flag(acc, wave, lane);
+  if (F16) f16_flag(acc, g.M, wave, lane);
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < R; ++r)

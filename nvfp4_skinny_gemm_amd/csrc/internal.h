@@ -254,8 +254,9 @@ struct nvfp4v_ctx {
 // Context status lines: 8 lines of DEV_LINE_WORDS words, line x holding the
 // row blocks begun and completed on XCD x by split-K GEMMs that exchange
 // through one XCD's L2 (the two totals differ only if a row block's pieces
-// ran on two XCDs).
-constexpr int DEV_LINE_WORDS = 32, DEV_ROWS_BEGUN = 0, DEV_ROWS_DONE = 1;
+// ran on two XCDs), and the GEMM work units on XCD x computed again from the
+// bf16 copy of their activations after meeting a marker in the fp16 copy.
+constexpr int DEV_LINE_WORDS = 32, DEV_ROWS_BEGUN = 0, DEV_ROWS_DONE = 1, DEV_F16_REDONE = 2;
 constexpr size_t DEV_STATUS_BYTES = 8 * DEV_LINE_WORDS * sizeof(unsigned);
 
 // Timeline capacity: 2 stamps for each of up to 1024 work-groups and 512 phases.

@@ -126,6 +126,9 @@ def test_other_argument_errors(lib):
     buf = ctypes.create_string_buffer(8)
     assert lib.nvfp4v_describe_plan(ctx, 16, 128, 0, buf, 8) == nv.E_M_RANGE
     assert lib.nvfp4v_device_status(None) == nv.E_INVALID_ARG
+    n = ctypes.c_uint64(0)
+    assert lib.nvfp4v_f16_redone(None, ctypes.byref(n)) == nv.E_INVALID_ARG
+    assert lib.nvfp4v_f16_redone(ctx, None) == nv.E_INVALID_ARG
     assert nv.strerror(nv.E_DISPATCH) != "unknown status"
 
 

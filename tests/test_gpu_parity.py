@@ -524,7 +524,14 @@ def test_fp16_copy_gives_bf16_results(torch_cuda, ctx, oracle_mod, monkeypatch, 
         a_dev = bf16_dev(torch, a)
         for m in ms:
             log("fp16 copy, plan %s, %s, M=%d: %s" % (plan, name, m, ctx.describe_plan(n, k, m)))
+            redone = ctx.f16_redone()
             c16 = ctx.verify_gemm(a_dev[:m].contiguous(), packed, n, k, ts=1.5)
+            redone = ctx.f16_redone() - redone
+            has_marker = bool((f16_copy_expected(a[:m]) == 0x7FFF).any())
+            if name == "nonfinite":  # infinities can make NaN sums without a marker
+                assert redone > 0 or not has_marker, (plan, name, m)
+            else:
+                assert (redone > 0) == has_marker, (plan, name, m, redone)
             monkeypatch.setenv("NVFP4V_F16", "0")
             cbf = ctx.verify_gemm(a_dev[:m].contiguous(), packed, n, k, ts=1.5)
             monkeypatch.delenv("NVFP4V_F16")

@@ -442,3 +442,33 @@ def test_full_stack_stays_finite_and_bounded(torch_cuda, mode_ctx):
     rms = t.pow(2).mean(dim=(1, 2)).sqrt().cpu().numpy()
     log("rms by layer: first %.3f last %.3f max %.3f" % (rms[0], rms[-1], rms.max()))
     assert rms.max() < 8.0 and rms.min() > 0.125
+
+
+@pytest.mark.parametrize("m", [12, 40])
+def test_padding_rows_leave_the_fp16_path(torch_cuda, ctx, m):
+    """The staged GEMM variants (activations through LDS) read whole 16-row
+    blocks, so the rows beyond M hold whatever the workspace held. With NaN
+    bit patterns there (a workspace filled with 0xFF) the pass gives the same
+    h as on a zeroed workspace, bitwise, and no unit falls back to the bf16
+    copy unless the activations themselves carry a marker (M = 12: gate|up
+    and down staged; M = 40: o staged, three row blocks)."""
+    torch = torch_cuda
+    H, I, L = 5120, 17408, 2
+    packed, arr = small_stack(torch, ctx, L, H, I, seed=4)
+    a0 = synth.activations_bf16(64, H, seed=0, stream="pass/h0")
+    h0 = torch.from_numpy(a0.view(np.int16)).cuda().view(torch.bfloat16)
+    outs, redone = [], []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((nv.pass_workspace_bytes(m, H, I, L),), fill, dtype=torch.uint8, device="cuda")
+        h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+        before = ctx.f16_redone()
+        ctx.verify_pass(arr, H, I, h0[:m], ws, h_out)
+        redone.append(ctx.f16_redone() - before)
+        outs.append(h_out.view(torch.int16).cpu().numpy())
+        C, acts, acts16 = workspace_views(ws.cpu().numpy(), m, H, I, L)
+        markers = sum(int((unpack_act(acts16[l][j], m, kk) == 0x7FFF).sum())
+                      for l in range(L) for j, kk in enumerate((H, H, H, I)))
+        log("M=%d fill 0x%02X: %d units recomputed, %d markers" % (m, fill, redone[-1], markers))
+        if markers == 0:
+            assert redone[-1] == 0, (m, fill, redone[-1])
+    assert np.array_equal(outs[0], outs[1]), m
