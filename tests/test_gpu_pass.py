@@ -472,3 +472,33 @@ def test_padding_rows_leave_the_fp16_path(torch_cuda, ctx, m):
         if markers == 0:
             assert redone[-1] == 0, (m, fill, redone[-1])
     assert np.array_equal(outs[0], outs[1]), m
+
+
+@pytest.mark.parametrize("m", [8, 24, 40])
+def test_pass_with_markers_equals_composition(torch_cuda, ctx, m):
+    """Values of h0 outside the fp16 copy's exact range (tiny, large, bf16
+    subnormal) become markers in the first layer's input; its launches then
+    test their sums and compute those units again from the bf16 copy. The
+    pass still equals the composition of single calls bitwise, run after run
+    (the marker words are cleared between passes), and a following pass
+    without markers recomputes nothing."""
+    torch = torch_cuda
+    H, I, L = 256, 512, 3
+    packed, arr = small_stack(torch, ctx, L, H, I)
+    base = synth.activations_bf16(128, H, seed=3)
+    marked = base.copy()
+    g = np.random.default_rng(m)
+    specials = (np.array([1e-12, -3e-9, 300.0, -1e5], np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    for r in range(m):
+        marked[r, g.choice(H, 2, replace=False)] = g.choice(np.concatenate([specials, [0x0001]]).astype(np.uint16), 2)
+    ws = torch.empty(nv.pass_workspace_bytes(m, H, I, L), dtype=torch.uint8, device="cuda")
+    h_out = torch.empty((m, H), dtype=torch.bfloat16, device="cuda")
+    for name, a in (("marked", marked), ("marked again", marked), ("plain", base)):
+        h0 = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        before = ctx.f16_redone()
+        ctx.verify_pass(arr, H, I, h0[:m], ws, h_out)
+        redone = ctx.f16_redone() - before
+        ref = manual_chain(torch, ctx, packed, h0[:m], H, I)
+        log("M=%d %s: %d units recomputed" % (m, name, redone))
+        assert torch.equal(h_out.view(torch.int16), ref[-1].view(torch.int16)), (m, name)
+        assert (redone > 0) == (name != "plain"), (m, name, redone)
