@@ -290,11 +290,12 @@ def test_plan_variants(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
 
 @pytest.mark.parametrize("plan", ["r=4,ks=1", "r=4,ks=3", "r=4,ks=18"])
 def test_two_deep_activation_ring(torch_cuda, ctx, oracle_mod, monkeypatch, plan):
-    """Two row blocks at R = 4 take the one-deep weight ring with two-deep
-    activation fragments: each wave sums its k-tiles in the same order as the
-    plain one-deep ring (NVFP4V_A2=0), so C is bitwise the same, and it agrees
-    with the oracle (odd and even k-tile counts per wave, one k-tile per
-    work-group at 18 pieces, ragged row tiles)."""
+    """One and two row blocks at R = 4 take the one-deep weight ring with
+    two-deep activation fragments: each wave sums its k-tiles in the same
+    order as the plain rings (NVFP4V_A2=0: two-deep at one row block, one-deep
+    at two), so C is bitwise the same, and it agrees with the oracle (odd and
+    even k-tile counts per wave, one k-tile per work-group at 18 pieces,
+    ragged row tiles)."""
     torch = torch_cuda
     n, k = 272, 4608
     g = np.random.default_rng(47)
@@ -304,7 +305,7 @@ def test_two_deep_activation_ring(torch_cuda, ctx, oracle_mod, monkeypatch, plan
     packed = pack_dev(torch, ctx, codes, scales, n, k)
     a_dev = bf16_dev(torch, a)
     monkeypatch.setenv("NVFP4V_PLAN", plan)
-    for m in (17, 24, 32):
+    for m in (1, 9, 16, 17, 24, 32):
         monkeypatch.setenv("NVFP4V_A2", "1")
         c2 = ctx.verify_gemm(a_dev[:m], packed, n, k, ts=0.75)
         monkeypatch.setenv("NVFP4V_A2", "0")
