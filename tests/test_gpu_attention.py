@@ -228,3 +228,4 @@ def test_argument_errors(torch_cuda, ctx):
     assert call(ws_bytes=100) == nv.E_WORKSPACE
     assert call(qp=ctypes.c_void_p(q.data_ptr() + 2)) == nv.E_ALIGN
     torch.cuda.synchronize()
+
