@@ -73,10 +73,10 @@ void k_gemm(GemmArgs g) {
   if ((int)blockIdx.x >= g.nrb) return;  // grid padding
   if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
   const int ks = blockIdx.y, kA = ks * g.kts_per_split, kB = min(g.nkt, kA + g.kts_per_split);
-  if constexpr (MB <= F16_MAX_MB) {
-    if (g.act16 && gemm_unit<MB, R, D, A2, true>(g, blockIdx.x, kA, kB, ks, g.ksplit, red)) return;
-    count_f16_redone(g);
-  }
+  // Every kernel carries both paths (its registers are the larger path's):
+  // the fp16 copy first, the bf16 copy for a unit that met a marker.
+  if (g.act16 && gemm_unit<MB, R, D, A2, true>(g, blockIdx.x, kA, kB, ks, g.ksplit, red)) return;
+  count_f16_redone(g);
   gemm_unit<MB, R, D, A2, false>(g, blockIdx.x, kA, kB, ks, g.ksplit, red);
 }
 
@@ -91,10 +91,8 @@ void k_gemm_lds(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
   if ((int)blockIdx.x >= g.nrb) return;  // grid padding
   if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
-  if constexpr (MB <= F16_MAX_MB) {
-    if (g.act16 && gemm_unit_lds<MB, R, true>(g, blockIdx.x, blockIdx.y, lds)) return;
-    count_f16_redone(g);
-  }
+  if (g.act16 && gemm_unit_lds<MB, R, true>(g, blockIdx.x, blockIdx.y, lds)) return;
+  count_f16_redone(g);
   gemm_unit_lds<MB, R, false>(g, blockIdx.x, blockIdx.y, lds);
 }
 
@@ -105,10 +103,8 @@ void k_gemm_wide(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
   if ((int)blockIdx.x >= g.nrb) return;  // grid padding
   if (g.xcd_local && blockIdx.y == 0 && threadIdx.x == 0) count_row_block(g.status, DEV_ROWS_BEGUN);
-  if constexpr (F16_WIDE) {
-    if (g.act16 && gemm_unit_wide<MB, R, true>(g, blockIdx.x, blockIdx.y, lds)) return;
-    count_f16_redone(g);
-  }
+  if (g.act16 && gemm_unit_wide<MB, R, true>(g, blockIdx.x, blockIdx.y, lds)) return;
+  count_f16_redone(g);
   gemm_unit_wide<MB, R, false>(g, blockIdx.x, blockIdx.y, lds);
 }
 

@@ -129,11 +129,6 @@ __device__ inline uint16_t f16_act_bits(uint16_t bf) {
   return exact ? u : ACT_F16_MARK;
 }
 
-// Which kernels carry the fp16-copy path besides the bf16 one (both are
-// compiled into the kernel, so its registers are the larger path's).
-constexpr int F16_MAX_MB = 8;       // register and LDS variants: row blocks up to this
-constexpr bool F16_WIDE = true;     // the wide-M unit
-
 // End of a unit computed from the fp16 copy, in two steps around the
 // work-group barrier that follows the sums' write to LDS. f16_flag (every
 // wave, before the barrier): scales its sums back by 2^-ACT_F16_SHIFT (exact)
