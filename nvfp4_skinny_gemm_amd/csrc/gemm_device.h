@@ -69,10 +69,10 @@ __device__ inline void scales4(uint32_t sw, float s[4]) {
 }
 
 // The fp16 dequantisation: two E2M1 codes -> fp16 (unit scale), times the
-// block scale as fp16 (ss: the scale in both halves) in one packed multiply. E4M3 scales are exact in fp16
-// (2^-9 is an fp16 normal), and so are their products with E2M1 values (at
-// most 6 significant bits in [2^-10, 2688]): one VALU operation per weight
-// against two for the bf16 form.
+// block scale as fp16 (ss: the scale in both halves) in one packed multiply.
+// E4M3 scales are exact in fp16 (2^-9 is an fp16 normal), and so are their
+// products with E2M1 values (at most 6 significant bits in [2^-10, 2688]):
+// one VALU operation per weight against two for the bf16 form.
 __device__ inline f16x8 dequant8h(uint32_t codes, f16x2 ss) {
   const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss;
   const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
