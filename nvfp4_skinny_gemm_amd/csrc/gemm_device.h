@@ -753,13 +753,25 @@ __device__ inline bool gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
   f32x4 *red = reinterpret_cast<f32x4 *>(lds + 2 * SLOT);
 
   // Staging: k-tile j's packed block is contiguous (SLOT bytes at j * SLOT);
-  // thread t moves chunks t, t + 256, ... of it.
+  // thread t moves chunks x = t, t + 256, ... of it. Chunk x holds row
+  // 16 (x >> 9) + (x & 15) (fragment x >> 6, lane x & 63). With one row block
+  // a row >= M gets an offset of OOB, so its loads return zeros without a
+  // memory access (at M = 1 that skips 15 of every 16); with more, at most
+  // 15 of 32 or more rows are padding and every chunk is loaded (rows >= M
+  // then hold whatever the buffer holds; the marker test ignores them).
+  // Offsets are unsigned 32-bit: the largest, OOB + OOB, does not wrap.
+  uint32_t lo[PER_THREAD];
+#pragma unroll
+  for (int c = 0; c < PER_THREAD; ++c) {
+    const int x = c * WG_THREADS + tid;
+    lo[c] = MB > 1 || (x & 15) < g.M ? (uint32_t)x * 16 : (uint32_t)OOB;
+  }
   auto stage_load = [&](uint4 (&v)[PER_THREAD], int j) {
-    const int base = j < n ? (kA + j) * SLOT : OOB;
+    const uint32_t base = j < n ? (uint32_t)((kA + j) * SLOT) : (uint32_t)OOB;
 #pragma unroll
     for (int c = 0; c < PER_THREAD; ++c) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(ra, base + (c * WG_THREADS + tid) * 16, 0, 0);
-      __builtin_memcpy(&v[c], &x, 16);
+      const auto y = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(base + lo[c]), 0, 0);
+      __builtin_memcpy(&v[c], &y, 16);
     }
   };
   auto stage_store = [&](const uint4 (&v)[PER_THREAD], int slot) {
@@ -777,7 +789,6 @@ __device__ inline bool gemm_unit_lds(const GemmArgs &g, int rb, int ks, uint8_t 
         __builtin_memcpy(&b[mb][q], &x, 16);
       }
   };
-  // Rows >= M read zeros from the packed block (the packer wrote zeros there).
 
   f32x4 acc[R][MB];
 #pragma unroll
