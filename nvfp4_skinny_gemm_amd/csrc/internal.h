@@ -49,7 +49,10 @@ struct Layout {
 //   ((kt * MB + mb) * 8 + q) * 1024
 // whose lane L = col + 16 h holds 8 values A[16 mb + col][256 kt + 64 h + 8 q + e],
 // e = 0..7 (MB = ceil(M / 16)). A wave reads one fragment with one fully
-// coalesced 16-byte load per lane. Rows >= M are never read.
+// coalesced 16-byte load per lane. Rows >= M are read only where a work-group
+// stages whole blocks (the verify GEMM's staged variants with two or more
+// row blocks, the FP8 head), and their sums are never stored; every other
+// loader gets zeros for them from an out-of-range offset.
 //
 // The packed form holds two copies of A in this order: the bf16 values, and
 // `act16` bytes further on (the size of one copy) the same values as fp16
