@@ -251,7 +251,7 @@ def kernel_source_hash():
     """sha256 over the verify GEMM's device sources (the traffic figure in
     profiles/ is valid only for the kernel it was taken on)."""
     h = hashlib.sha256()
-    for f in ("csrc/gemm.hip", "csrc/gemm_device.h", "tables/gfx950.txt"):
+    for f in ("csrc/gemm.hip", "csrc/gemm_device.h", "csrc/internal.h", "tables/gfx950.txt"):
         h.update(open(os.path.join(ROOT, "nvfp4_skinny_gemm_amd", f), "rb").read())
     return h.hexdigest()
 
