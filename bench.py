@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 H, I, LAYERS = 5120, 17408, 64
+PROFILED_M = 16  # M of the committed rocprofv3 counter summaries
 BYTES_PER_WEIGHT = 0.5625  # 4-bit code + one E4M3 byte per 16 weights
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense fp16 and bf16 MFMA (the same peak)
@@ -704,9 +705,10 @@ def main():
     check_device(ctx, nv, "roofline GEMMs")
     achieved = gbytes / (gms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = traffic_from_profile(src_hash)
     avg_us = gms * 1e3 / launches
-    mfma_util, valu_util = utilisation(src_hash, avg_us)
+    # The committed counter summaries were taken at M = 16: other M report none.
+    traffic = traffic_from_profile(src_hash) if args.m == PROFILED_M else None
+    mfma_util, valu_util = utilisation(src_hash, avg_us) if args.m == PROFILED_M else (None, None)
     mfma_tflops = sum(v["mfma_TFLOPs"] * v["us"] for v in per_shape.values()) / sum(v["us"] for v in per_shape.values())
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
