@@ -249,6 +249,21 @@ def test_staircase_runs(ctx):
     assert us.shape == (4,) and (us > 0).all()
 
 
+def test_staircase_steps_at_second_row_block(ctx):
+    """A10 on the square layer shape (5120 x 5120, weight copies rotated over
+    1 GiB so every launch streams from HBM): the cost is flat within the first
+    16-row block and rises once the 17th row opens a second block, where every
+    wave reads two activation fragments per k-tile (StairCut research page,
+    abstract: the verify cost moves in steps at tile boundaries; release post,
+    the staircase paragraph). Measured margins: +17-21 % at the step, the
+    first block within 1.2x of itself."""
+    us = ctx.staircase(5120, 5120, 1, 24, warmup=2, reps=7, rotate_bytes=1 << 30)
+    assert us.shape == (24,) and (us > 0).all()
+    first, second = float(us[8:16].mean()), float(us[16:24].mean())
+    assert second > 1.05 * first, us
+    assert float(us[:16].max()) < 1.5 * float(us[:16].min()), us
+
+
 def test_prepacked_activations_match(torch_cuda, ctx):
     """verify_gemm_pa on pack_activations output equals verify_gemm, bitwise."""
     torch = torch_cuda
