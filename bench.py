@@ -350,9 +350,11 @@ def staircase_report(ctx, m_hi=64, reps=7):
 def summarize_staircase_trace(csv_path, m_hi=64, reps=7):
     """Per-M kernel durations of a `--staircase-only` run from its rocprofv3
     kernel trace (CSV): dispatches in start order; each shape's sweep begins
-    with its fill kernel, each M with its activation-packing kernel, followed by
-    STAIR_WARMUP + STAIR_ROUNDS * reps GEMM launches, of which the timed ones
-    are kept. Returns {shape: {"us": [median per M], "steps": [...]}}."""
+    with its fill kernel and one activation-packing kernel followed by an
+    untimed launch per weight copy, then each M with its activation-packing
+    kernel, followed by STAIR_WARMUP + STAIR_ROUNDS * reps GEMM launches, of
+    which the timed ones are kept. Returns {shape: {"us": [median per M],
+    "steps": [...]}}."""
     import csv
     import re
     import statistics
@@ -377,6 +379,7 @@ def summarize_staircase_trace(csv_path, m_hi=64, reps=7):
     out = {}
     timed = STAIR_ROUNDS * reps
     for (name, n, k), groups in zip(STAIR_SHAPES, sections):
+        groups = groups[1:]  # the untimed rotation over the weight copies
         assert len(groups) == m_hi, "%s: %d row counts in the trace" % (name, len(groups))
         us = []
         for g in groups:
