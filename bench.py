@@ -594,8 +594,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is "
-              "described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the weight rows "
+              "would shard by column, or by K with one all-reduce per row-parallel projection); "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.summarize_attention_trace:
         paths = args.summarize_attention_trace
